@@ -1,0 +1,96 @@
+"""The seeded input generators: bf16 rounding, e4m3 block quantization,
+rotation, outlier channels, row subsets, determinism."""
+import numpy as np
+import torch
+
+import oracle
+from exact_tiled_attention_15_amd import configs, inputs
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        rng.standard_normal(100000).astype(np.float32) * 10,
+        # exact ties between two bf16 values: mantissa low half = 0x8000
+        (np.arange(1000, dtype=np.uint32) << 16 | 0x8000).view(np.float32),
+        np.array([0.0, -0.0, 1e-40, -3e38, 3e38], dtype=np.float32),
+    ])
+    got = inputs.bf16_bits(x)
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, want)
+    np.testing.assert_array_equal(inputs.bf16_bits_to_f32(got),
+                                  torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def _e4m3_table():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = np.array([oracle.e4m3_value(int(c)) for c in codes])
+    return codes, vals
+
+
+def test_e4m3_quantizer_is_nearest_even_per_tile():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((1, 2, 300, 16)).astype(np.float32)
+    x[0, 0, :, 3] *= 20.0
+    codes, scales = inputs.quantize_e4m3_tiles(x, 128)
+    assert scales.shape == (1, 2, 3)
+    tcodes, tvals = _e4m3_table()
+    for h in range(2):
+        for t in range(3):
+            blk = x[0, h, t * 128:(t + 1) * 128]
+            s = np.float32(np.abs(blk).max() / 448.0)
+            assert scales[0, h, t] == s
+            y = np.clip((blk / s).astype(np.float32), -448, 448).astype(np.float64).ravel()
+            c = codes[0, h, t * 128:(t + 1) * 128].ravel()
+            got = np.array([oracle.e4m3_value(int(ci)) for ci in c])
+            dist = np.abs(y[:, None] - tvals[None, :])
+            best = dist.min(axis=1)
+            # the chosen code is a nearest representable value ...
+            np.testing.assert_array_equal(np.abs(y - got), best)
+            # ... and on a tie it has an even mantissa
+            ties = (dist == best[:, None]).sum(axis=1) > 1
+            for ci in c[ties]:
+                assert (int(ci) & 1) == 0 or (int(ci) & 0x7F) == 0
+    # the tile maximum maps to +-448 exactly
+    assert np.max(np.abs([oracle.e4m3_value(int(ci)) for ci in codes[0, 0, :128].ravel()])) == 448.0
+
+
+def test_e4m3_quantizer_zero_tile_scale_one():
+    x = np.zeros((1, 1, 128, 8), dtype=np.float32)
+    codes, scales = inputs.quantize_e4m3_tiles(x)
+    assert scales[0, 0, 0] == 1.0 and np.all(codes == 0)
+
+
+def test_rotation_orthogonal_and_preserves_scores():
+    m = inputs.rotation(128, 7)
+    np.testing.assert_allclose(m @ m.T, np.eye(128), atol=1e-12)
+    rng = np.random.default_rng(2)
+    q, k = rng.standard_normal((20, 128)), rng.standard_normal((30, 128))
+    np.testing.assert_allclose((q @ m) @ (k @ m).T, q @ k.T, atol=1e-10)
+    assert not np.allclose(inputs.rotation(128, 8), m)
+
+
+def test_fp8_workload_outliers_shared_by_qkv():
+    cfg = dict(configs.WORKLOADS["fp8_B4_H16_N4096_d128"], B=1, H=1, Nq=256, Nk=256)
+    x = inputs.make_inputs(cfg, 1004)
+    ch = x["channels"]
+    assert len(ch) == max(1, round(0.01 * 128)) == 1
+    for name in ("q_unquantized", "k_unquantized", "v_unquantized"):
+        t = x[name][0, 0]
+        col = np.abs(t).mean(axis=0)
+        assert np.argmax(col) == ch[0] and col[ch[0]] > 10 * np.median(col)
+
+
+def test_row_subset_and_determinism():
+    r = inputs.row_subset(32768, 512, 1002)
+    assert len(r) == 512 and len(np.unique(r)) == 512 and r.min() >= 0 and r.max() < 32768
+    np.testing.assert_array_equal(r, inputs.row_subset(32768, 512, 1002))
+    np.testing.assert_array_equal(inputs.row_subset(10, 512, 1), np.arange(10))
+    a = inputs.normal_f32((3, 4), 5, 0)
+    np.testing.assert_array_equal(a, inputs.normal_f32((3, 4), 5, 0))
+    assert not np.array_equal(a, inputs.normal_f32((3, 4), 5, 1))
+
+
+def test_flop_convention():
+    assert configs.flops(8, 16, 2048, 2048, 128, True) == 4 * 8 * 16 * 2048 * 2048 * 128 / 2
+    assert configs.flops(1, 16, 8192, 65536, 128, False) == 4 * 16 * 8192 * 65536 * 128

@@ -1,0 +1,254 @@
+"""Pins of the fp64 oracle against things other than itself: a decimal brute
+force of the definition, hand-derived closed forms (tests/golden), invariants
+that follow from the definition, the block-merge identity, and the decoders
+against torch's own dtypes."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.brute_decimal import attention_decimal
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
+
+
+def _num(x):
+    return -math.inf if x == "-inf" else float(x)
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+# ---------------------------------------------------------------- brute force
+@pytest.mark.parametrize("Nq,Nk,d,causal", [
+    (1, 1, 1, False), (3, 5, 2, False), (5, 5, 3, True), (4, 7, 4, True),
+    (7, 3, 2, True), (8, 8, 4, False), (6, 2, 3, False), (2, 8, 1, True),
+])
+def test_oracle_matches_decimal_brute_force(Nq, Nk, d, causal):
+    rng = np.random.default_rng(Nq * 100 + Nk * 10 + d)
+    q = rng.standard_normal((1, 1, Nq, d)) * 2
+    k = rng.standard_normal((1, 1, Nk, d)) * 2
+    v = rng.standard_normal((1, 1, Nk, d))
+    scale = 0.8
+    o, lse = oracle.attention(q, k, v, causal, scale)
+    ob, lb = attention_decimal(q[0, 0], k[0, 0], v[0, 0], causal, scale)
+    np.testing.assert_allclose(o[0, 0], ob, rtol=0, atol=1e-12)
+    fin = np.isfinite(lb)
+    np.testing.assert_allclose(lse[0, 0][fin], lb[fin], rtol=0, atol=1e-12)
+    assert np.all(np.isneginf(lse[0, 0][~fin]))
+
+
+# -------------------------------------------------------------- closed forms
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("case", _golden()["attention"], ids=lambda c: c["name"])
+def test_oracle_closed_forms(case):
+    q = np.array(case["q"], dtype=np.float64)[None, None]
+    k = np.array(case["k"], dtype=np.float64)[None, None]
+    v = np.array(case["v"], dtype=np.float64)[None, None]
+    o, lse = oracle.attention(q, k, v, case["causal"], case["scale"])
+    np.testing.assert_allclose(o[0, 0], np.array(case["o"]), rtol=0, atol=1e-12)
+    want = np.array([_num(x) for x in case["lse"]])
+    fin = np.isfinite(want)
+    np.testing.assert_allclose(lse[0, 0][fin], want[fin], rtol=0, atol=1e-12)
+    assert np.all(np.isneginf(lse[0, 0][~fin]))
+
+
+@pytest.mark.parametrize("case", _golden()["merge"], ids=lambda c: c["name"])
+def test_merge_closed_forms(case):
+    def st(s):
+        return (np.array(s["o"], dtype=np.float64), np.array([_num(x) for x in s["m"]]),
+                np.array(s["l"], dtype=np.float64))
+    o, m, l = oracle.merge(st(case["a"]), st(case["b"]))
+    np.testing.assert_allclose(o, np.array(case["o"]), atol=1e-12)
+    np.testing.assert_allclose(m, [_num(x) for x in case["m"]], atol=1e-12)
+    np.testing.assert_allclose(l, case["l"], atol=1e-12)
+    np.testing.assert_allclose(oracle.state_lse(m, l), [_num(x) for x in case["lse"]], atol=1e-12)
+
+
+# ---------------------------------------------------------------- invariants
+def test_closed_form_two_keys_general():
+    # d = 1, two keys: O = sigma(s1 - s2) v1 + sigma(s2 - s1) v2.
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        qv, k1, k2, v1, v2 = rng.standard_normal(5) * 3
+        scale = rng.uniform(0.1, 2.0)
+        s1, s2 = scale * qv * k1, scale * qv * k2
+        sig = lambda x: 1.0 / (1.0 + math.exp(-x))
+        want = sig(s1 - s2) * v1 + sig(s2 - s1) * v2
+        o, lse = oracle.attention(np.array([[[[qv]]]]), np.array([[[[k1], [k2]]]]),
+                                  np.array([[[[v1], [v2]]]]), False, scale)
+        assert abs(o[0, 0, 0, 0] - want) < 1e-12
+        assert abs(lse[0, 0, 0] - (max(s1, s2) + math.log1p(math.exp(-abs(s1 - s2))))) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_probability_rows(causal):
+    B, H, Nq, Nk, d = 2, 3, 37, 41, 16
+    q, k, v = _rand((B, H, Nq, d), 1), _rand((B, H, Nk, d), 2), _rand((B, H, Nk, d), 3)
+    scale = 0.3
+    o, lse, p = oracle.attention(q, k, v, causal, scale, want_p=True)
+    # rows of P sum to one, P_ij = exp(s_ij - LSE_i) on the allowed keys, 0 elsewhere
+    np.testing.assert_allclose(p.sum(-1), 1.0, atol=1e-12)
+    s = scale * np.einsum("bhid,bhjd->bhij", q, k)
+    allowed = np.ones((Nq, Nk), dtype=bool)
+    if causal:
+        allowed = np.arange(Nk)[None, :] <= np.arange(Nq)[:, None] + Nk - Nq
+    want_p = np.where(allowed, np.exp(s - lse[..., None]), 0.0)
+    np.testing.assert_allclose(p, want_p, atol=1e-12)
+    np.testing.assert_allclose(o, p @ v, atol=1e-12)
+
+
+def test_single_key_returns_value():
+    q, k, v = _rand((2, 2, 9, 8), 4), _rand((2, 2, 1, 8), 5), _rand((2, 2, 1, 8), 6)
+    o, lse = oracle.attention(q, k, v, False, 0.5)
+    np.testing.assert_allclose(o, np.broadcast_to(v, o.shape), atol=0)
+    np.testing.assert_allclose(lse, 0.5 * np.einsum("bhid,bhjd->bhi", q, k), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_query_gives_mean(causal):
+    Nq, Nk = 6, 10
+    q, k, v = np.zeros((1, 2, Nq, 4)), _rand((1, 2, Nk, 4), 7), _rand((1, 2, Nk, 4), 8)
+    o, lse = oracle.attention(q, k, v, causal, 1.3)
+    for i in range(Nq):
+        n = (i + Nk - Nq + 1) if causal else Nk
+        np.testing.assert_allclose(o[:, :, i], v[:, :, :n].mean(axis=2), atol=1e-12)
+        np.testing.assert_allclose(lse[:, :, i], math.log(n), atol=1e-12)
+
+
+def test_constant_values_and_linearity_and_shift():
+    q, k = _rand((1, 2, 12, 8), 9), _rand((1, 2, 15, 8), 10)
+    v1, v2 = _rand((1, 2, 15, 8), 11), _rand((1, 2, 15, 8), 12)
+    const = np.broadcast_to(np.arange(8.0), (1, 2, 15, 8))
+    o, _ = oracle.attention(q, k, const, True, 0.7)
+    np.testing.assert_allclose(o, np.broadcast_to(np.arange(8.0), o.shape), atol=1e-12)
+    o1, _ = oracle.attention(q, k, v1, False, 0.7)
+    o2, _ = oracle.attention(q, k, v2, False, 0.7)
+    o12, _ = oracle.attention(q, k, 2.0 * v1 - 3.0 * v2, False, 0.7)
+    np.testing.assert_allclose(o12, 2.0 * o1 - 3.0 * o2, atol=1e-12)
+    # adding w to every key shifts row i's scores by scale*q_i.w: O unchanged, LSE shifted
+    w = _rand((8,), 13)
+    o_s, lse_s = oracle.attention(q, k + w, v1, False, 0.7)
+    _, lse_1 = oracle.attention(q, k, v1, False, 0.7)
+    np.testing.assert_allclose(o_s, o1, atol=1e-12)
+    np.testing.assert_allclose(lse_s, lse_1 + 0.7 * q @ w, atol=1e-12)
+
+
+def test_joint_key_value_permutation():
+    q, k, v = _rand((1, 1, 10, 6), 14), _rand((1, 1, 13, 6), 15), _rand((1, 1, 13, 6), 16)
+    perm = np.random.default_rng(17).permutation(13)
+    o, lse = oracle.attention(q, k, v, False, 0.9)
+    op, lsep = oracle.attention(q, k[:, :, perm], v[:, :, perm], False, 0.9)
+    np.testing.assert_allclose(op, o, atol=1e-12)
+    np.testing.assert_allclose(lsep, lse, atol=1e-12)
+
+
+def test_causal_first_row_sees_only_first_key():
+    q, k, v = _rand((1, 2, 8, 4), 18), _rand((1, 2, 8, 4), 19), _rand((1, 2, 8, 4), 20)
+    o, lse = oracle.attention(q, k, v, True, 0.6)
+    np.testing.assert_allclose(o[:, :, 0], v[:, :, 0], atol=0)
+    np.testing.assert_allclose(lse[:, :, 0], 0.6 * np.sum(q[:, :, 0] * k[:, :, 0], -1), atol=1e-12)
+    # the last row of a square causal problem sees every key
+    o_full, lse_full = oracle.attention(q, k, v, False, 0.6)
+    np.testing.assert_allclose(o[:, :, -1], o_full[:, :, -1], atol=1e-12)
+
+
+def test_row_subset_matches_full():
+    q, k, v = _rand((2, 2, 30, 8), 21), _rand((2, 2, 30, 8), 22), _rand((2, 2, 30, 8), 23)
+    rows = np.array([0, 3, 17, 29])
+    o, lse = oracle.attention(q, k, v, True, 0.5)
+    os_, lses = oracle.attention(q, k, v, True, 0.5, rows=rows)
+    np.testing.assert_array_equal(os_, o[:, :, rows])
+    np.testing.assert_array_equal(lses, lse[:, :, rows])
+
+
+# ------------------------------------------------------------ merge identity
+@pytest.mark.parametrize("splits", [[1, 20], [7, 3, 11], [3] * 7, [8] * 8, [1] * 9])
+def test_block_states_merge_to_one_pass(splits):
+    Nk = sum(splits)
+    q, k, v = _rand((1, 2, 9, 8), 24, 2.0), _rand((1, 2, Nk, 8), 25, 2.0), _rand((1, 2, Nk, 8), 26)
+    o, lse = oracle.attention(q, k, v, False, 0.6)
+    acc = oracle.empty_state(o.shape)
+    start = 0
+    for n in splits:
+        st = oracle.block_state(q, k[:, :, start:start + n], v[:, :, start:start + n], False, 0, start, 0.6)
+        acc = oracle.merge(acc, st)
+        start += n
+    np.testing.assert_allclose(acc[0], o, atol=1e-12)
+    np.testing.assert_allclose(oracle.state_lse(acc[1], acc[2]), lse, atol=1e-12)
+
+
+def test_causal_block_states_merge_to_one_pass():
+    # global positions: the local query shard sits at the end of the sequence
+    Nq, Nk, blk = 12, 40, 8
+    q, k, v = _rand((1, 1, Nq, 4), 27), _rand((1, 1, Nk, 4), 28), _rand((1, 1, Nk, 4), 29)
+    o, lse = oracle.attention(q, k, v, True, 0.9)  # bottom-right: q_pos0 = Nk - Nq
+    acc = oracle.empty_state(o.shape)
+    for s0 in range(0, Nk, blk):
+        st = oracle.block_state(q, k[:, :, s0:s0 + blk], v[:, :, s0:s0 + blk], True, Nk - Nq, s0, 0.9)
+        acc = oracle.merge(acc, st)
+    np.testing.assert_allclose(acc[0], o, atol=1e-12)
+    np.testing.assert_allclose(oracle.state_lse(acc[1], acc[2]), lse, atol=1e-12)
+
+
+def test_merge_commutative_associative_identity():
+    q = _rand((1, 1, 5, 4), 30)
+    ks = [_rand((1, 1, 6, 4), 31 + i, 2.0) for i in range(3)]
+    vs = [_rand((1, 1, 6, 4), 41 + i) for i in range(3)]
+    a, b, c = (oracle.block_state(q, ks[i], vs[i], False, 0, 6 * i, 1.1) for i in range(3))
+    ab, ba = oracle.merge(a, b), oracle.merge(b, a)
+    for x, y in zip(ab, ba):
+        np.testing.assert_allclose(x, y, atol=1e-12)
+    left, right = oracle.merge(oracle.merge(a, b), c), oracle.merge(a, oracle.merge(b, c))
+    for x, y in zip(left, right):
+        np.testing.assert_allclose(x, y, atol=1e-12)
+    e = oracle.empty_state(a[0].shape)
+    for x, y in zip(oracle.merge(a, e), a):
+        np.testing.assert_allclose(x, y, atol=1e-15)
+    for x, y in zip(oracle.merge(e, a), a):
+        np.testing.assert_allclose(x, y, atol=1e-15)
+
+
+def test_fully_masked_block_is_empty_state():
+    q, k, v = _rand((1, 1, 4, 4), 50), _rand((1, 1, 4, 4), 51), _rand((1, 1, 4, 4), 52)
+    o, m, l = oracle.block_state(q, k, v, True, 0, 10, 1.0)  # keys at 10..13, queries at 0..3
+    assert np.all(o == 0) and np.all(np.isneginf(m)) and np.all(l == 0)
+
+
+# ------------------------------------------------------------------ decoders
+def test_bf16_decode_matches_torch_for_every_pattern():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle.decode_bf16(bits.reshape(1, 1, -1, 1)).ravel()
+    want = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    np.testing.assert_array_equal(got[~nan], want[~nan])
+
+
+def test_e4m3_decode_matches_torch_for_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    got = np.array([oracle.e4m3_value(int(c)) for c in codes])
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(want)
+    assert nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+    assert np.array_equal(np.isnan(got), nan)
+    np.testing.assert_array_equal(got[~nan], want[~nan])
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
+
+
+def test_e4m3_decode_applies_tile_scales():
+    codes = np.full((1, 2, 300, 4), 0x38, dtype=np.uint8)  # 1.0
+    scales = np.array([[[0.5, 2.0, 3.0], [1.0, 4.0, 0.25]]], dtype=np.float32)
+    x = oracle.decode_e4m3(codes, scales, 128)
+    for h in range(2):
+        for n in range(300):
+            assert np.all(x[0, h, n] == scales[0, h, n // 128])
