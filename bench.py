@@ -1,0 +1,238 @@
+"""Benchmark of the attention forward on one MI355X.
+
+One step = one pass of the hot path over one batch of synthetic input:
+  * attn_fwd over the whole batch (bf16 workloads without K/V blocks),
+  * attn_fwd_f32 (fp32 workload), attn_fwd_fp8 (fp8 workload),
+  * n_blocks x attn_fwd_kvblock plus the merges (block-streamed workload).
+W untimed warm-up steps, then K steps back to back on one stream, bracketed
+by HIP events recorded on that stream (torch.cuda.Event on the stream the
+kernels are launched on) and device synchronisation.  Inputs are resident in
+HBM before the timed region starts.  Prints one JSON line.
+
+The default workload is the causal bf16 B=8 H=16 N=2048 d=128 attention
+(TFLOP/s = 4*B*H*N^2*d/2 / time).  The CPU baseline is the fp64 oracle timed
+on a bounded sample of the same workload (whole heads, all rows).
+"""
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+REPO = os.path.dirname(os.path.abspath(__file__))
+if REPO not in sys.path:
+    sys.path.insert(0, REPO)
+
+PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}  # dense MFMA, 256 CU x 2.4 GHz
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain copy kernel of known size (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the path shards by (batch, head) and by ring hops, which no run here exercises.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_tiled_attention_15_amd as eta
+    from exact_tiled_attention_15_amd import configs, inputs
+
+    name = args.workload or configs.HEADLINE
+    cfg = configs.WORKLOADS[name]
+    seed = configs.seed_of(name)
+    B, H, Nq, Nk, d = cfg["B"], cfg["H"], cfg["Nq"], cfg["Nk"], cfg["d"]
+    causal = cfg["causal"]
+    scale = configs.scale_of(name)
+    dtype = cfg["dtype"]
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    x = inputs.make_inputs(cfg, seed)
+    bf = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
+    dv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    if dtype == "bf16" and "n_blocks" not in cfg:
+        q, k, v = bf(x["q"]), bf(x["k"]), bf(x["v"])
+        o = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((B, H, Nq), device="cuda")
+        step = lambda: eta.attn_fwd(q, k, v, o, lse, causal, scale, stream)
+        kernel = "fwd_bf16_kernel"
+        launches = 1
+    elif dtype == "bf16":
+        nb = cfg["n_blocks"]
+        blk = Nk // nb
+        q, k, v = bf(x["q"]), bf(x["k"]), bf(x["v"])
+        kbs = [k[:, :, i * blk:(i + 1) * blk].contiguous() for i in range(nb)]
+        vbs = [v[:, :, i * blk:(i + 1) * blk].contiguous() for i in range(nb)]
+        del k, v
+        acc = [torch.empty((B, H, Nq, d), device="cuda"), torch.empty((B, H, Nq), device="cuda"),
+               torch.empty((B, H, Nq), device="cuda")]
+        part = [torch.empty_like(t) for t in acc]
+        o = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((B, H, Nq), device="cuda")
+
+        def step():
+            eta.attn_fwd_kvblock(q, kbs[0], vbs[0], *acc, False, 0, 0, scale, stream)
+            for i in range(1, nb):
+                eta.attn_fwd_kvblock(q, kbs[i], vbs[i], *part, False, 0, i * blk, scale, stream)
+                last = i == nb - 1
+                eta.attn_merge(*acc, *part, o if last else None, lse if last else None, stream)
+        kernel = "fwd_bf16_kernel (state epilogue) + merge_kernel"
+        launches = nb
+    elif dtype == "f32":
+        q, k, v = dv(x["q"]), dv(x["k"]), dv(x["v"])
+        o = torch.empty((B, H, Nq, d), device="cuda")
+        lse = torch.empty((B, H, Nq), device="cuda")
+        step = lambda: eta.attn_fwd_f32(q, k, v, o, lse, causal, scale, stream)
+        kernel = "fwd_f32_kernel"
+        launches = 1
+    else:
+        t = {n: dv(x[n]) for n in ("q8", "k8", "v8", "q_scale", "k_scale", "v_scale")}
+        o = torch.empty((B, H, Nq, d), device="cuda")
+        lse = torch.empty((B, H, Nq), device="cuda")
+        step = lambda: eta.attn_fwd_fp8(t["q8"], t["k8"], t["v8"], t["q_scale"], t["k_scale"], t["v_scale"],
+                                        o, lse, causal, scale, stream)
+        kernel = "fwd_fp8_kernel"
+        launches = 1
+
+    flop = configs.flops(B, H, Nq, Nk, d, causal)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+    tflops = flop / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[dtype]
+
+    if args.copy_calibration:
+        # plain copy of a known size: 256 MiB read + 256 MiB written
+        src = torch.ones(64 << 20, device="cuda")
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+
+    roofline = {
+        "bound": "mfma",
+        "kernel": kernel,
+        "achieved": round(tflops, 2),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(tflops / peak, 4),
+        "traffic": None,
+        "launches_per_step": launches,
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(name, cfg, seed, x, args.cpu_seconds)
+
+    out = {
+        "metric": "attention fwd TFLOP/s (bf16 d=128, causal) and % of MI355X dense MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded N(0,1) inputs of the workload's shape)",
+        "config": {"workload": name, "B": B, "H": H, "Nq": Nq, "Nk": Nk, "d": d, "causal": causal,
+                   "scale": scale, "seed": seed},
+        "pct_of_peak": round(100 * tflops / peak, 2),
+        "wall_s_timed": round(t_wall, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(name, cfg, seed, x, target_s):
+    """The fp64 oracle on whole heads of the same workload, sized to ~target_s."""
+    import oracle
+    from exact_tiled_attention_15_amd import configs
+
+    B, H, Nq, Nk, d, causal = cfg["B"], cfg["H"], cfg["Nq"], cfg["Nk"], cfg["d"], cfg["causal"]
+    scale = configs.scale_of(name)
+    dtype = cfg["dtype"]
+
+    def head(b, h):
+        if dtype == "bf16":
+            dec = lambda a: oracle.decode_bf16(a[b:b + 1, h:h + 1])
+            return dec(x["q"]), dec(x["k"]), dec(x["v"])
+        if dtype == "f32":
+            return tuple(x[n][b:b + 1, h:h + 1].astype(np.float64) for n in ("q", "k", "v"))
+        dq = lambda c, s: oracle.decode_e4m3(c[b:b + 1, h:h + 1], s[b:b + 1, h:h + 1])
+        return dq(x["q8"], x["q_scale"]), dq(x["k8"], x["k_scale"]), dq(x["v8"], x["v_scale"])
+
+    # Size the sample with one probe of 32 rows, then run whole heads.
+    q, k, v = head(0, 0)
+    probe_rows = np.arange(Nq - 32, Nq, dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, causal, scale, rows=probe_rows)
+    t_probe = time.perf_counter() - t0
+    keys_probe = float(sum((i + Nk - Nq + 1) if causal else Nk for i in probe_rows))
+    keys_head = float(sum((i + Nk - Nq + 1) if causal else Nk for i in range(Nq)))
+    t_head = max(t_probe * keys_head / keys_probe, 1e-6)
+    n_heads = int(max(1, min(B * H, target_s / t_head)))
+    flop = 0.0
+    elapsed = 0.0  # oracle time only; decoding the slice's inputs is not counted
+    for u in range(n_heads):
+        b, h = divmod(u, H)
+        q, k, v = head(b, h)
+        tt = time.perf_counter()
+        oracle.attention(q, k, v, causal, scale)
+        elapsed += time.perf_counter() - tt
+        flop += 4.0 * d * keys_head
+    return {
+        "value": round(flop / elapsed / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{n_heads} of {B * H} (b,h) slices, all {Nq} rows x {'causal' if causal else 'all'} keys, "
+                  f"fp64, {elapsed:.1f} s on {cpu_model()}",
+        "flop": flop,
+        "seconds": round(elapsed, 3),
+    }
+
+
+if __name__ == "__main__":
+    main()

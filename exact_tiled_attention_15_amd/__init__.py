@@ -1,1 +1,24 @@
-"""Exact, IO-aware attention forward for AMD Instinct MI355X (gfx950)."""
+"""Exact, IO-aware attention forward for AMD Instinct MI355X (gfx950).
+
+The compute lives in libattn.so (hand-written HIP kernels behind the C ABI of
+include/attn.h); this package is its thin Python binding plus the seeded
+synthetic-input generators and workload table used by the tests and the
+benchmark.
+"""
+from ._lib import (  # noqa: F401
+    ATTN_ERR_HIP,
+    ATTN_ERR_INVALID,
+    ATTN_ERR_UNSUPPORTED,
+    ATTN_OK,
+    FP8_TILE,
+    AttnError,
+    abi_version,
+    attn_fwd,
+    attn_fwd_f32,
+    attn_fwd_fp8,
+    attn_fwd_fp8_qk16,
+    attn_fwd_kvblock,
+    attn_merge,
+    lib,
+    status_str,
+)

@@ -1,0 +1,188 @@
+"""ctypes binding of libattn.so (include/attn.h).
+
+Argument marshalling only: every function here checks that the torch tensors
+it is handed have the dtype/shape/device the C entry point documents, passes
+their device pointers and sizes, and raises AttnError on a non-zero status.
+All computation happens in the library's HIP kernels.  There is no fallback:
+if libattn.so is missing or cannot be loaded, every call raises.
+"""
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+ATTN_OK = 0
+ATTN_ERR_INVALID = 1
+ATTN_ERR_UNSUPPORTED = 2
+ATTN_ERR_HIP = 3
+FP8_TILE = 128
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libattn.so once; raise loudly when it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python exact_tiled_attention_15_amd/build.py`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64
+    L.attn_abi_version.restype = i
+    L.attn_abi_version.argtypes = []
+    L.attn_status_str.restype = ctypes.c_char_p
+    L.attn_status_str.argtypes = [i]
+    L.attn_fwd.restype = i
+    L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    L.attn_fwd_f32.restype = i
+    L.attn_fwd_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    L.attn_fwd_kvblock.restype = i
+    L.attn_fwd_kvblock.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i64, i64, f, vp]
+    L.attn_merge.restype = i
+    L.attn_merge.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
+    for name in ("attn_fwd_fp8", "attn_fwd_fp8_qk16"):
+        fn = getattr(L, name)
+        fn.restype = i
+        fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    _lib = L
+    return L
+
+
+def _check(status: int, what: str):
+    if status != ATTN_OK:
+        raise AttnError(status, f"{what}: {lib().attn_status_str(status).decode()}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _want(t, dtype, shape, name):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+
+
+def abi_version() -> int:
+    return lib().attn_abi_version()
+
+
+def status_str(s: int) -> str:
+    return lib().attn_status_str(s).decode()
+
+
+def attn_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None):
+    """q [B,H,Nq,d], k/v [B,H,Nk,d], o [B,H,Nq,d] bf16; lse [B,H,Nq] fp32 or None."""
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    _want(q, torch.bfloat16, (B, H, Nq, d), "q")
+    _want(k, torch.bfloat16, (B, H, Nk, d), "k")
+    _want(v, torch.bfloat16, (B, H, Nk, d), "v")
+    _want(o, torch.bfloat16, (B, H, Nq, d), "o")
+    if lse is not None:
+        _want(lse, torch.float32, (B, H, Nq), "lse")
+    _check(lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
+                          int(bool(causal)), float(scale), _stream(stream)), "attn_fwd")
+
+
+def attn_fwd_f32(q, k, v, o, lse, causal: bool, scale: float, stream=None):
+    """As attn_fwd with float32 q/k/v/o."""
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    _want(q, torch.float32, (B, H, Nq, d), "q")
+    _want(k, torch.float32, (B, H, Nk, d), "k")
+    _want(v, torch.float32, (B, H, Nk, d), "v")
+    _want(o, torch.float32, (B, H, Nq, d), "o")
+    if lse is not None:
+        _want(lse, torch.float32, (B, H, Nq), "lse")
+    _check(lib().attn_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
+                              int(bool(causal)), float(scale), _stream(stream)), "attn_fwd_f32")
+
+
+def attn_fwd_kvblock(q, k_blk, v_blk, o_part, m_part, l_part, causal: bool, q_pos0: int,
+                     k_pos0: int, scale: float, stream=None):
+    """Partial state of q against one K/V block: o_part fp32, m_part/l_part fp32 [B,H,Nq]."""
+    B, H, Nq, d = q.shape
+    Nkb = k_blk.shape[2]
+    _want(q, torch.bfloat16, (B, H, Nq, d), "q")
+    _want(k_blk, torch.bfloat16, (B, H, Nkb, d), "k_blk")
+    _want(v_blk, torch.bfloat16, (B, H, Nkb, d), "v_blk")
+    _want(o_part, torch.float32, (B, H, Nq, d), "o_part")
+    _want(m_part, torch.float32, (B, H, Nq), "m_part")
+    _want(l_part, torch.float32, (B, H, Nq), "l_part")
+    _check(lib().attn_fwd_kvblock(_ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(o_part), _ptr(m_part),
+                                  _ptr(l_part), B, H, Nq, Nkb, d, int(bool(causal)), int(q_pos0),
+                                  int(k_pos0), float(scale), _stream(stream)), "attn_fwd_kvblock")
+
+
+def attn_merge(o_acc, m_acc, l_acc, o_part, m_part, l_part, o_final=None, lse_final=None,
+               stream=None):
+    """Merge a block state into the accumulator (in place); optional bf16 O / LSE outputs."""
+    B, H, Nq, d = o_acc.shape
+    _want(o_acc, torch.float32, (B, H, Nq, d), "o_acc")
+    _want(m_acc, torch.float32, (B, H, Nq), "m_acc")
+    _want(l_acc, torch.float32, (B, H, Nq), "l_acc")
+    _want(o_part, torch.float32, (B, H, Nq, d), "o_part")
+    _want(m_part, torch.float32, (B, H, Nq), "m_part")
+    _want(l_part, torch.float32, (B, H, Nq), "l_part")
+    if o_final is not None:
+        _want(o_final, torch.bfloat16, (B, H, Nq, d), "o_final")
+    if lse_final is not None:
+        _want(lse_final, torch.float32, (B, H, Nq), "lse_final")
+    _check(lib().attn_merge(_ptr(o_acc), _ptr(m_acc), _ptr(l_acc), _ptr(o_part), _ptr(m_part),
+                            _ptr(l_part), _ptr(o_final), _ptr(lse_final), B, H, Nq, d,
+                            _stream(stream)), "attn_merge")
+
+
+def _fwd_fp8(entry, q8, k8, v8, q_scale, k_scale, v_scale, o, lse, causal, scale, stream):
+    B, H, Nq, d = q8.shape
+    Nk = k8.shape[2]
+    nqt = (Nq + FP8_TILE - 1) // FP8_TILE
+    nkt = (Nk + FP8_TILE - 1) // FP8_TILE
+    _want(q8, torch.uint8, (B, H, Nq, d), "q8")
+    _want(k8, torch.uint8, (B, H, Nk, d), "k8")
+    _want(v8, torch.uint8, (B, H, Nk, d), "v8")
+    _want(q_scale, torch.float32, (B, H, nqt), "q_scale")
+    _want(k_scale, torch.float32, (B, H, nkt), "k_scale")
+    _want(v_scale, torch.float32, (B, H, nkt), "v_scale")
+    _want(o, torch.float32, (B, H, Nq, d), "o")
+    if lse is not None:
+        _want(lse, torch.float32, (B, H, Nq), "lse")
+    fn = getattr(lib(), entry)
+    _check(fn(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _ptr(o), _ptr(lse),
+              B, H, Nq, Nk, d, int(bool(causal)), float(scale), _stream(stream)), entry)
+
+
+def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, causal: bool, scale: float,
+                 stream=None):
+    """e4m3 codes (uint8) with fp32 per-128-token-tile scales; QK^T on fp8 matrix cores."""
+    _fwd_fp8("attn_fwd_fp8", q8, k8, v8, q_scale, k_scale, v_scale, o, lse, causal, scale, stream)
+
+
+def attn_fwd_fp8_qk16(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, causal: bool, scale: float,
+                      stream=None):
+    """As attn_fwd_fp8 with QK^T on fp16 matrix cores over exactly widened codes."""
+    _fwd_fp8("attn_fwd_fp8_qk16", q8, k8, v8, q_scale, k_scale, v_scale, o, lse, causal, scale, stream)

@@ -1,0 +1,192 @@
+// C ABI of libattn.so: argument validation on the host, then kernel dispatch.
+// Nothing here allocates device memory or synchronises; every check happens
+// before the first HIP call, so a rejected call has no side effect.
+#include "attn.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "common.h"
+
+namespace {
+
+using eta::FwdParams;
+
+constexpr int64_t kMaxTokens = int64_t(1) << 30;  // keeps every in-kernel token index in int
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+attn_status check_shape(int B, int H, int Nq, int Nk, int d) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return ATTN_ERR_INVALID;
+  if (Nq > kMaxTokens || Nk > kMaxTokens) return ATTN_ERR_INVALID;
+  const int64_t BH = int64_t(B) * H;
+  const int64_t nqb = (int64_t(Nq) + eta::kBM - 1) / eta::kBM;
+  if (BH * nqb > INT32_MAX) return ATTN_ERR_INVALID;  // grid size
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+attn_status check_ptrs16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!p || !aligned(p, 16)) return ATTN_ERR_INVALID;
+  return ATTN_OK;
+}
+
+attn_status check_ptrs4(std::initializer_list<const void*> ps, bool nullable) {
+  for (const void* p : ps) {
+    if (!p) {
+      if (!nullable) return ATTN_ERR_INVALID;
+      continue;
+    }
+    if (!aligned(p, 4)) return ATTN_ERR_INVALID;
+  }
+  return ATTN_OK;
+}
+
+FwdParams base_params(int B, int H, int Nq, int Nk, float scale) {
+  FwdParams p{};
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.BH = B * H;
+  p.nqb = (Nq + eta::kBM - 1) / eta::kBM;
+  p.diag = Nk - Nq;
+  const double a = std::fabs(double(scale));
+  p.scale_abs = float(a);
+  p.c = float(a * 1.4426950408889634074);  // log2(e)
+  p.q_sign = std::signbit(scale) && scale != 0.f ? 0x80008000u : 0u;
+  return p;
+}
+
+attn_status from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+const char* attn_status_str(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID: return "ATTN_ERR_INVALID: invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: unsupported configuration";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP: HIP runtime error at launch";
+  }
+  return "unknown attn_status";
+}
+
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                     int Nq, int Nk, int d, int causal, float scale, void* stream) {
+  if (attn_status s = check_shape(B, H, Nq, Nk, d)) return s;
+  if (attn_status s = check_ptrs16({q, k, v, o})) return s;
+  if (attn_status s = check_ptrs4({lse}, true)) return s;
+  if (!std::isfinite(scale)) return ATTN_ERR_INVALID;
+  FwdParams p = base_params(B, H, Nq, Nk, scale);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  return from_hip(eta::launch_fwd_bf16(p, d, causal != 0, eta::kEpiFinalBf16, (hipStream_t)stream));
+}
+
+attn_status attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
+                         int H, int Nq, int Nk, int d, int causal, float scale, void* stream) {
+  if (attn_status s = check_shape(B, H, Nq, Nk, d)) return s;
+  if (attn_status s = check_ptrs16({q, k, v, o})) return s;
+  if (attn_status s = check_ptrs4({lse}, true)) return s;
+  if (!std::isfinite(scale)) return ATTN_ERR_INVALID;
+  FwdParams p = base_params(B, H, Nq, Nk, scale);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  return from_hip(eta::launch_fwd_f32(p, d, causal != 0, (hipStream_t)stream));
+}
+
+attn_status attn_fwd_kvblock(const void* q, const void* k_blk, const void* v_blk, float* o_part,
+                             float* m_part, float* l_part, int B, int H, int Nq, int Nk_blk, int d,
+                             int causal, int64_t q_pos0, int64_t k_pos0, float scale, void* stream) {
+  if (attn_status s = check_shape(B, H, Nq, Nk_blk, d)) return s;
+  if (attn_status s = check_ptrs16({q, k_blk, v_blk, o_part})) return s;
+  if (attn_status s = check_ptrs4({m_part, l_part}, false)) return s;
+  if (!std::isfinite(scale)) return ATTN_ERR_INVALID;
+  if (causal && (q_pos0 < 0 || k_pos0 < 0)) return ATTN_ERR_INVALID;
+  FwdParams p = base_params(B, H, Nq, Nk_blk, scale);
+  // Key j allowed for row i iff k_pos0 + j <= q_pos0 + i, i.e. j <= i + diag.
+  // Clamping diag to [-Nq, Nk] keeps every allowed set unchanged.
+  int64_t diag = q_pos0 - k_pos0;
+  if (diag > Nk_blk) diag = Nk_blk;
+  if (diag < -int64_t(Nq)) diag = -int64_t(Nq);
+  p.diag = int(diag);
+  p.q = q;
+  p.k = k_blk;
+  p.v = v_blk;
+  p.o = o_part;
+  p.m_out = m_part;
+  p.l_out = l_part;
+  return from_hip(eta::launch_fwd_bf16(p, d, causal != 0, eta::kEpiState, (hipStream_t)stream));
+}
+
+attn_status attn_merge(float* o_acc, float* m_acc, float* l_acc, const float* o_part,
+                       const float* m_part, const float* l_part, void* o_final, float* lse_final,
+                       int B, int H, int Nq, int d, void* stream) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || d <= 0) return ATTN_ERR_INVALID;
+  if (d % 4 != 0 || d > 1024) return ATTN_ERR_UNSUPPORTED;
+  if (attn_status s = check_ptrs16({o_acc, o_part})) return s;
+  if (attn_status s = check_ptrs4({m_acc, l_acc, m_part, l_part}, false)) return s;
+  if (attn_status s = check_ptrs4({lse_final}, true)) return s;
+  if (o_final && !aligned(o_final, 8)) return ATTN_ERR_INVALID;
+  const int64_t rows = int64_t(B) * H * Nq;
+  const int vpr = d / 4;
+  const int rpb = vpr >= 256 ? 1 : 256 / vpr;
+  if ((rows + rpb - 1) / rpb > INT32_MAX) return ATTN_ERR_INVALID;
+  if (o_acc == o_part || m_acc == m_part || l_acc == l_part) return ATTN_ERR_INVALID;
+  eta::MergeParams p{};
+  p.o_acc = o_acc;
+  p.m_acc = m_acc;
+  p.l_acc = l_acc;
+  p.o_part = o_part;
+  p.m_part = m_part;
+  p.l_part = l_part;
+  p.o_final = o_final;
+  p.lse_final = lse_final;
+  p.rows = rows;
+  p.d = d;
+  return from_hip(eta::launch_merge(p, (hipStream_t)stream));
+}
+
+static attn_status fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
+                           const float* k_scale, const float* v_scale, float* o, float* lse, int B, int H,
+                           int Nq, int Nk, int d, int causal, float scale, void* stream, bool qk16) {
+  if (attn_status s = check_shape(B, H, Nq, Nk, d)) return s;
+  if (attn_status s = check_ptrs16({q8, k8, v8, o})) return s;
+  if (attn_status s = check_ptrs4({q_scale, k_scale, v_scale}, false)) return s;
+  if (attn_status s = check_ptrs4({lse}, true)) return s;
+  if (!std::isfinite(scale)) return ATTN_ERR_INVALID;
+  FwdParams p = base_params(B, H, Nq, Nk, scale);
+  p.q = q8;
+  p.k = k8;
+  p.v = v8;
+  p.q_scale = q_scale;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.o = o;
+  p.lse = lse;
+  return from_hip(eta::launch_fwd_fp8(p, d, causal != 0, qk16, (hipStream_t)stream));
+}
+
+attn_status attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
+                         const float* k_scale, const float* v_scale, float* o, float* lse, int B, int H,
+                         int Nq, int Nk, int d, int causal, float scale, void* stream) {
+  return fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, Nq, Nk, d, causal, scale, stream, false);
+}
+
+attn_status attn_fwd_fp8_qk16(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
+                              const float* k_scale, const float* v_scale, float* o, float* lse, int B, int H,
+                              int Nq, int Nk, int d, int causal, float scale, void* stream) {
+  return fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, Nq, Nk, d, causal, scale, stream, true);
+}
+
+}  // extern "C"

@@ -1,0 +1,173 @@
+/*
+ * attn.h - C ABI of libattn.so: exact, IO-aware softmax attention forward on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes O = softmax(scale * Q K^T [+ causal mask]) V together
+ * with the per-row log-sum-exp, tile by tile with an online softmax, so the
+ * Nq x Nk score matrix never reaches device memory.  The operation is standard
+ * softmax attention, reached exactly up to floating-point rounding
+ * ("FlashAttention-2", Systems analysis wiki: lead paragraph, "Background: the
+ * attention problem in transformers", "Technical architecture and working
+ * principles"); the block-wise state merge is the online softmax of
+ * "Sequence parallelism and ring attention" (aiunderstanding.org, "Deep dive",
+ * "Technical insight"); the fp8 entry point takes the block-quantized inputs
+ * of "Scaling FlashAttention, multi-GPU training and weight quantization"
+ * (itimpress, section 1, FP8 bullet).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
+ *    allocates nothing, keeps no global state, and never synchronises the host:
+ *    each call validates its arguments on the host, enqueues its kernels on
+ *    `stream` (a hipStream_t; NULL means the default stream) and returns.
+ *  - Layout: contiguous [B, H, N, d] row-major, d innermost; per-row outputs
+ *    (lse, m, l) are contiguous [B, H, N].  Q/K/V/O pointers must be 16-byte
+ *    aligned; per-row pointers 4-byte aligned.  Outputs must not alias inputs.
+ *  - d must be 64 or 128.  B, H, N >= 1.  `scale` must be finite (any sign;
+ *    0 gives uniform weights).
+ *  - Scores are s_ij = scale * q_i . k_j.  With `causal` set, query row i may
+ *    attend key j iff j <= i + (Nk - Nq) (bottom-right aligned; j <= i when
+ *    Nq == Nk).  A row with no allowed key gets O = 0 and lse = -inf.
+ *  - lse_i = ln sum_j exp(s_ij) over the allowed keys (natural log, includes
+ *    scale), in fp32.
+ *  - Errors: arguments are checked before anything is enqueued.  A failed
+ *    check returns ATTN_ERR_INVALID (null pointer, non-positive size,
+ *    misalignment, non-finite scale, size overflow) or ATTN_ERR_UNSUPPORTED
+ *    (a d other than 64/128) and launches nothing, writes nothing.  If the HIP
+ *    runtime reports an error at launch, ATTN_ERR_HIP is returned; outputs are
+ *    then undefined.  Kernel faults surface at the caller's next
+ *    synchronisation, as for any HIP kernel.
+ *  - Results are deterministic: the same inputs give bit-identical outputs
+ *    (no atomics, fixed reduction order).
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+/* Tokens per quantization tile of attn_fwd_fp8 scales. */
+#define ATTN_FP8_TILE 128
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID = 1,
+    ATTN_ERR_UNSUPPORTED = 2,
+    ATTN_ERR_HIP = 3
+} attn_status;
+
+/* Constant ATTN_ABI_VERSION of the built library. */
+int attn_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* attn_status_str(attn_status s);
+
+/*
+ * attn_fwd - one pass over all keys, bfloat16 in, bfloat16 out.
+ *   q   bf16 [B,H,Nq,d]     k, v  bf16 [B,H,Nk,d]
+ *   o   bf16 [B,H,Nq,d]     O = P V with P = softmax of the allowed scores,
+ *                           accumulated in fp32, rounded to nearest-even once.
+ *   lse fp32 [B,H,Nq]       may be NULL (not written).
+ * The outer loop runs over 128-row query blocks (one workgroup each, spread
+ * over all compute units: sequence-length parallelism); the inner loop streams
+ * 64-key K/V tiles through LDS, keeps the running max / normaliser per row and
+ * divides by the normaliser once after the loop ("FlashAttention-2", Systems
+ * analysis wiki, "Technical architecture and working principles", items 1-3).
+ * Causal key tiles above the diagonal are skipped wholesale.
+ */
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                     void* stream);
+
+/*
+ * attn_fwd_f32 - as attn_fwd with float32 q/k/v/o (fp32 matrix-core products,
+ * fp32 probabilities).  lse may be NULL.
+ */
+attn_status attn_fwd_f32(const float* q, const float* k, const float* v, float* o,
+                         float* lse, int B, int H, int Nq, int Nk, int d, int causal,
+                         float scale, void* stream);
+
+/*
+ * attn_fwd_kvblock - partial attention of the local queries against one block
+ * of keys/values: the per-hop compute of ring attention on one GPU
+ * ("Sequence parallelism and ring attention", "Deep dive", "Technical insight").
+ *   q       bf16 [B,H,Nq,d]           k_blk, v_blk  bf16 [B,H,Nk_blk,d]
+ *   o_part  fp32 [B,H,Nq,d]  O of the block, normalised by its own l
+ *   m_part  fp32 [B,H,Nq]    max_j s_ij over the block's allowed keys
+ *                            (natural units, includes scale); -inf if none
+ *   l_part  fp32 [B,H,Nq]    sum_j exp(s_ij - m_part); 0 if no key allowed
+ * q_pos0 / k_pos0 are the global token positions of query row 0 and of the
+ * block's key 0; with `causal` set key j is allowed for row i iff
+ * k_pos0 + j <= q_pos0 + i (ignored when causal == 0).  A row with no allowed
+ * key gets the empty state (O = 0, m = -inf, l = 0), the identity of
+ * attn_merge.
+ */
+attn_status attn_fwd_kvblock(const void* q, const void* k_blk, const void* v_blk,
+                             float* o_part, float* m_part, float* l_part,
+                             int B, int H, int Nq, int Nk_blk, int d, int causal,
+                             int64_t q_pos0, int64_t k_pos0, float scale, void* stream);
+
+/*
+ * attn_merge - online-softmax merge of a block state into an accumulated
+ * state, in place:  M = max(m_acc, m_part); w_x = l_x exp(m_x - M);
+ * o_acc = (w_acc o_acc + w_part o_part) / (w_acc + w_part); l_acc = w_acc +
+ * w_part; m_acc = M.  The empty state (m = -inf, l = 0) is the identity.
+ *   o_acc, o_part  fp32 [B,H,Nq,d]     m_*, l_*  fp32 [B,H,Nq]
+ *   o_final        bf16 [B,H,Nq,d] or NULL: if given, also receives the
+ *                  merged O rounded to bf16
+ *   lse_final      fp32 [B,H,Nq] or NULL: if given, receives M + ln l
+ *                  (-inf for the empty state)
+ * The accumulator is always updated.  To start an accumulation, either
+ * write the first block's attn_fwd_kvblock output straight into the
+ * accumulator, or initialise m = -inf, l = 0, o = 0.
+ * o_acc/m_acc/l_acc may not alias the *_part buffers.  Here d may be any
+ * multiple of 4 in [4, 1024].
+ */
+attn_status attn_merge(float* o_acc, float* m_acc, float* l_acc,
+                       const float* o_part, const float* m_part, const float* l_part,
+                       void* o_final, float* lse_final,
+                       int B, int H, int Nq, int d, void* stream);
+
+/*
+ * attn_fwd_fp8 - attention on block-quantized OCP FP8 E4M3 ("e4m3fn") inputs
+ * ("Scaling FlashAttention, multi-GPU training and weight quantization",
+ * itimpress, section 1, FP8 bullet: a separate scale per small tile).
+ *   q8   u8 [B,H,Nq,d]   k8, v8  u8 [B,H,Nk,d]      e4m3 codes
+ *   q_scale fp32 [B,H,ceil(Nq/128)]   k_scale, v_scale fp32 [B,H,ceil(Nk/128)]
+ *        the value of element x of token n is code(x) * scale[b,h,n/128]
+ *   o    fp32 [B,H,Nq,d]     lse fp32 [B,H,Nq] or NULL
+ * Q K^T runs on fp8 matrix cores; P V runs with P in fp16 against V codes
+ * converted exactly to fp16; O is kept and written in fp32.
+ * The fp8 matrix cores sum the products of one instruction with limited
+ * alignment precision, so a channel whose products dwarf the others (an
+ * outlier channel) perturbs the scores; the same passage's remedy,
+ * "incoherent processing" (Q and K multiplied by one random orthogonal
+ * matrix before quantization), removes such channels.  attn_fwd_fp8_qk16
+ * below is exact for any codes.
+ * Scales must be finite and > 0; NaN codes (0x7F, 0xFF) give undefined output.
+ */
+attn_status attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                         const float* q_scale, const float* k_scale, const float* v_scale,
+                         float* o, float* lse, int B, int H, int Nq, int Nk, int d,
+                         int causal, float scale, void* stream);
+
+/*
+ * attn_fwd_fp8_qk16 - attn_fwd_fp8 with Q K^T on fp16 matrix cores over the
+ * codes widened exactly to fp16 (exact products, fp32 sums), for
+ * block-quantized inputs that were not rotated.  Same arguments, layout and
+ * outputs as attn_fwd_fp8; the fp8 storage (half the bytes of bf16) is kept.
+ */
+attn_status attn_fwd_fp8_qk16(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                              const float* q_scale, const float* k_scale, const float* v_scale,
+                              float* o, float* lse, int B, int H, int Nq, int Nk, int d,
+                              int causal, float scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,97 @@
+"""CPU-side checks of the C ABI: the built library exports every function
+include/attn.h declares, and rejects invalid arguments on the host (before
+any HIP call, so these run without a GPU).  No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_tiled_attention_15_amd as eta
+
+REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(REPO, "include", "attn.h")
+
+P16 = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation
+P16b = ctypes.c_void_p(0x20000)
+P16c = ctypes.c_void_p(0x30000)
+P16d = ctypes.c_void_p(0x40000)
+P4 = ctypes.c_void_p(0x50004)
+MIS = ctypes.c_void_p(0x60008)   # 8-byte aligned only
+NUL = None
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"attn_fwd", "attn_fwd_f32", "attn_fwd_kvblock", "attn_merge", "attn_fwd_fp8",
+            "attn_abi_version", "attn_status_str"} <= set(names)
+    L = eta.lib()
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported by libattn.so"
+
+
+def test_version_and_status_strings():
+    assert eta.abi_version() == 1
+    for s in range(4):
+        assert eta.status_str(s).startswith("ATTN_")
+    assert "unknown" in eta.status_str(99)
+
+
+def fwd(*, q=P16, k=P16b, v=P16c, o=P16d, lse=NUL, B=1, H=1, Nq=8, Nk=8, d=64, causal=0, scale=0.125):
+    return eta.lib().attn_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=NUL), eta.ATTN_ERR_INVALID),
+    (dict(o=NUL), eta.ATTN_ERR_INVALID),
+    (dict(B=0), eta.ATTN_ERR_INVALID),
+    (dict(H=-1), eta.ATTN_ERR_INVALID),
+    (dict(Nq=0), eta.ATTN_ERR_INVALID),
+    (dict(Nk=0), eta.ATTN_ERR_INVALID),
+    (dict(d=0), eta.ATTN_ERR_INVALID),
+    (dict(d=96), eta.ATTN_ERR_UNSUPPORTED),
+    (dict(d=256), eta.ATTN_ERR_UNSUPPORTED),
+    (dict(k=MIS), eta.ATTN_ERR_INVALID),
+    (dict(lse=ctypes.c_void_p(0x50002)), eta.ATTN_ERR_INVALID),
+    (dict(scale=float("nan")), eta.ATTN_ERR_INVALID),
+    (dict(scale=float("inf")), eta.ATTN_ERR_INVALID),
+    (dict(Nq=(1 << 30) + 1), eta.ATTN_ERR_INVALID),
+    (dict(B=1 << 16, H=1 << 16, Nq=1024), eta.ATTN_ERR_INVALID),  # grid > 2^31 in 64-bit math
+])
+def test_attn_fwd_validation(kw, want):
+    assert fwd(**kw) == want
+
+
+def test_f32_and_fp8_validation():
+    L = eta.lib()
+    assert L.attn_fwd_f32(P16, P16b, P16c, NUL, NUL, 1, 1, 8, 8, 64, 0, 0.1, None) == eta.ATTN_ERR_INVALID
+    assert L.attn_fwd_f32(P16, P16b, P16c, P16d, NUL, 1, 1, 8, 8, 32, 0, 0.1, None) == eta.ATTN_ERR_UNSUPPORTED
+    fp8 = lambda qs, ks, vs, d=128: L.attn_fwd_fp8(P16, P16b, P16c, qs, ks, vs, P16d, NUL, 1, 1, 8, 8, d, 0,
+                                                   0.1, None)
+    assert fp8(NUL, P4, P4) == eta.ATTN_ERR_INVALID
+    assert fp8(P4, P4, ctypes.c_void_p(0x50001)) == eta.ATTN_ERR_INVALID
+    assert fp8(P4, P4, P4, d=80) == eta.ATTN_ERR_UNSUPPORTED
+
+
+def test_kvblock_and_merge_validation():
+    L = eta.lib()
+    kv = lambda m, l, causal=0, qp=0, kp=0: L.attn_fwd_kvblock(P16, P16b, P16c, P16d, m, l, 1, 1, 8, 8, 64,
+                                                               causal, qp, kp, 0.1, None)
+    assert kv(NUL, P4) == eta.ATTN_ERR_INVALID
+    assert kv(P4, NUL) == eta.ATTN_ERR_INVALID
+    assert kv(P4, P4, causal=1, qp=-1) == eta.ATTN_ERR_INVALID
+    assert kv(P4, P4, causal=1, kp=-5) == eta.ATTN_ERR_INVALID
+    mg = lambda oa, op, d=128, of=NUL, ma=P4, mp=ctypes.c_void_p(0x70004): L.attn_merge(
+        oa, ma, ctypes.c_void_p(0x80004), op, mp, ctypes.c_void_p(0x90004), of, NUL, 1, 1, 8, d, None)
+    assert mg(NUL, P16b) == eta.ATTN_ERR_INVALID
+    assert mg(P16, P16b, d=130) == eta.ATTN_ERR_UNSUPPORTED
+    assert mg(P16, P16b, d=2048) == eta.ATTN_ERR_UNSUPPORTED
+    assert mg(P16, P16) == eta.ATTN_ERR_INVALID            # o_acc aliases o_part
+    assert mg(P16, P16b, ma=P4, mp=P4) == eta.ATTN_ERR_INVALID  # m_acc aliases m_part
+    assert mg(P16, P16b, of=ctypes.c_void_p(0x50002)) == eta.ATTN_ERR_INVALID
