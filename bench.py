@@ -29,6 +29,37 @@ if REPO not in sys.path:
 
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}  # dense MFMA, 256 CU x 2.4 GHz
 
+# rocprofv3 FETCH_SIZE/WRITE_SIZE summaries (copy-calibrated) per workload; the
+# figure is reported only while the kernel sources still hash to the value the
+# counters were taken with.
+TRAFFIC_PROFILES = {
+    "bf16_causal_B8_H16_N2048_d128": "profiles/fwd_bf16_causal_B8_H16_N2048_d128_hbm_traffic.txt",
+}
+
+
+def measured_traffic(workload):
+    import hashlib
+
+    path = TRAFFIC_PROFILES.get(workload)
+    if not path or not os.path.exists(os.path.join(REPO, path)):
+        return None
+    fields = {}
+    with open(os.path.join(REPO, path)) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    try:
+        h = hashlib.sha256()
+        for src in fields["kernel sources"].split():
+            with open(os.path.join(REPO, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != fields["kernel_source_sha256"]:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -154,7 +185,8 @@ def main():
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(tflops / peak, 4),
-        "traffic": None,
+        "traffic": measured_traffic(name),
+        "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
         "launches_per_step": launches,
     }
 
