@@ -52,8 +52,17 @@ FwdParams base_params(int B, int H, int Nq, int Nk, float scale) {
   p.diag = Nk - Nq;
   const double a = std::fabs(double(scale));
   p.scale_abs = float(a);
-  p.c = float(a * 1.4426950408889634074);  // log2(e)
-  p.q_sign = std::signbit(scale) && scale != 0.f ? 0x80008000u : 0u;
+  if (scale == 0.f) {
+    // Every score is 0: run as Q = 0 with a positive exponent factor, so masked
+    // keys still get exp2(-inf) = 0.
+    p.c = 1.f;
+    p.q_and = 0u;
+    p.q_xor = 0u;
+  } else {
+    p.c = float(a * 1.4426950408889634074);  // log2(e)
+    p.q_and = 0xFFFFFFFFu;
+    p.q_xor = scale < 0.f ? 0x80008000u : 0u;  // sign bit of each 16-bit element
+  }
   return p;
 }
 

@@ -21,12 +21,17 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // -------------------------------------------------------------- tile geometry
-// One workgroup = 4 wavefronts = 128 query rows (32 per wavefront); each inner
-// iteration consumes 64 keys.
+// Every wavefront owns 32 query rows; a workgroup of kWaves wavefronts owns
+// kBM rows (the bf16 kernel uses its own, larger workgroups); each inner
+// iteration consumes kBN keys.
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;
 constexpr int kBN = 64;
+// bf16 forward: 8 wavefronts = 256 query rows per workgroup, one workgroup per
+// compute unit, 128-key tiles; every K/V tile staged into LDS serves 256 rows.
+constexpr int kWavesBf16 = 8;
+constexpr int kTileBf16 = 128;
 
 // What the epilogue of the forward kernels writes.
 enum Epilogue : int {
@@ -50,11 +55,15 @@ struct FwdParams {
   float* l_out;  // state epilogue
   int Nq, Nk;
   int BH;        // B * H
-  int nqb;       // ceil(Nq / kBM)
+  int nqb;       // query blocks per (b,h) slice: ceil(Nq / rows per workgroup), set by the launcher
   int diag;      // causal: key j allowed for row i iff j <= i + diag
-  float c;       // |scale| * log2(e): raw dot product -> base-2 exponent
+  float c;       // |scale| * log2(e) (> 0): raw dot product -> base-2 exponent
   float scale_abs;
-  uint32_t q_sign;  // sign mask xor-ed into Q elements when scale < 0
+  // Q element bits are replaced by (bits & q_and) ^ q_xor (mask for 16-bit
+  // lanes, repeated): flips Q's sign when scale < 0 so that c > 0, and zeroes Q
+  // when scale == 0 (all scores 0, the same problem as Q = 0).
+  uint32_t q_and;
+  uint32_t q_xor;
 };
 
 // Launchers (host side). Each returns hipGetLastError() after the launch.
@@ -78,10 +87,11 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t s);
 
 // ------------------------------------------------------------ device helpers
 // Workgroup -> (query block, b*h slice).  Workgroups are dealt to the 8 XCDs
-// round-robin (XCD = blockIdx % 8); when the work divides evenly, each XCD is
-// given a contiguous range of (b,h) slices so that one slice's K/V stays in one
-// XCD's L2.  For causal masks the heaviest query blocks (the last ones) are
-// issued first.
+// round-robin (XCD = blockIdx % 8); when the slices divide evenly, each XCD is
+// given a contiguous range of (b,h) slices, so a slice's K/V is only ever
+// cached in one XCD's L2.  Inside an XCD the order is query-block level by
+// level, heaviest level first for causal masks (longest-processing-time-first
+// list scheduling of blocks whose lengths differ by up to Nk/kBN tiles).
 __device__ inline void map_block(int g, int nqb, int BH, bool causal, int& qb, int& bh) {
   int qi;
   if ((BH & 7) == 0) {
@@ -109,5 +119,35 @@ __device__ inline float halves_sum(float x) {
 }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------- V^T tile
+// The P.V product reads V with keys along the MFMA k dimension, i.e. 8 keys of
+// one column d per lane.  V is therefore staged into LDS transposed: one LDS row
+// per column d, holding the tile's keys as 16-bit values.  Inside every
+// 16-key group the keys are stored in the order that makes the 8 keys one lane
+// needs for one MFMA adjacent: key 16q + 8a + 4g + b sits in slot
+// 16q + 8g + 4a + b (bits 2 and 3 of the key index swapped), matching the keys
+// the S^T accumulator hands each lane (rows 8*(i/4) + 4*(l/32) + i%4).  So one
+// ds_read_b128 fetches a whole A fragment.  The row pitch (tile keys + 16
+// bytes) keeps both the 16-byte reads down 32 consecutive rows and the 8-byte
+// writes of the staging free of bank conflicts.
+__host__ __device__ constexpr int vt_pitch(int bn) { return bn * 2 + 16; }
+constexpr int kVtPitch = vt_pitch(kBN);
+
+// Slot of key group kg (keys 4kg .. 4kg+3) inside a V^T row.
+__device__ inline int vt_slot(int kg) { return 16 * (kg >> 2) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1); }
+
+// Store four keys (w[r] = 8 consecutive 16-bit values of key 4kg + r, columns
+// d0 .. d0+7) into V^T rows d0 .. d0+7 of row pitch `pitch` bytes.
+__device__ inline void store_vt(char* vt, int pitch, int d0, int kg, const u32x4 (&w)[4]) {
+  const int col = vt_slot(kg) * 2;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int i = e >> 1;
+    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high / low halves
+    const u32x2 v = {__builtin_amdgcn_perm(w[1][i], w[0][i], sel), __builtin_amdgcn_perm(w[3][i], w[2][i], sel)};
+    *(u32x2*)(vt + (d0 + e) * pitch + col) = v;
+  }
+}
 
 }  // namespace eta

@@ -1,6 +1,6 @@
 // bf16 attention forward for gfx950: S^T = K Q^T and O^T += V^T P^T on
 // 32x32x16 bf16 MFMA, online softmax in registers, K/V tiles double-buffered
-// through LDS.
+// through LDS, and a software-pipelined tile loop.
 //
 // Structure follows "FlashAttention-2" (Systems analysis wiki, "Technical
 // architecture and working principles"): the outer loop is over query blocks
@@ -17,27 +17,41 @@
 // Computing S^T (rows = keys, columns = queries) leaves each lane with one
 // query's scores for 16 keys of a 32-key block, so row max / sum are in-lane
 // plus one permlane32 swap, and the scores feed O^T = V^T P^T as the B
-// operand without any data movement.  V^T fragments come from the row-major V
-// tile through ds_read_b64_tr_b16.
+// operand without any data movement.  The V^T fragments are single 16-byte
+// LDS reads from the transposed, key-permuted V tile (common.h).
+//
+// Staging.  A workgroup of W wavefronts owns 32*W query rows (W = 8: one
+// workgroup per compute unit, two wavefronts per SIMD), so every K/V tile read
+// from memory serves 256 rows.  K tiles go straight from global memory into LDS
+// (global_load_lds); V goes through registers so it can be stored transposed.
+// Tile t+1 is in flight while tile t is computed; one barrier per tile.
+//
+// Rescaling.  O and l are multiplied by alpha only on tiles where some row of
+// the wavefront raised its maximum (one ballot per tile).  The exponent always
+// uses the current maximum, so the dominant probability of a row is exp2 of a
+// rounding residual and rounds to exactly 1.0 in bf16.
 #include "common.h"
 
 namespace eta {
 
-template <int D>
+template <int D, int W, int BN>
 struct Geo {
-  static constexpr int ROW = D * 2;             // bytes in one bf16 row
-  static constexpr int KS = ROW + 16;           // K tile row pitch (bytes)
-  static constexpr int VS = ROW + 64;           // V tile row pitch (bytes)
-  static constexpr int K_BYTES = kBN * KS;
-  static constexpr int V_BYTES = kBN * VS;
-  static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int LDS = 2 * STAGE;         // double buffered
-  static constexpr int CPR = D / 8;             // 16-byte chunks per row
-  static constexpr int PER_THREAD = kBN * CPR / kThreads;
-  static_assert(PER_THREAD * kThreads == kBN * CPR, "tile must split evenly");
+  static constexpr int THREADS = 64 * W;
+  static constexpr int BM = 32 * W;           // query rows per workgroup
+  static constexpr int KB = BN / 32;          // 32-key blocks per tile
+  static constexpr int VTP = vt_pitch(BN);    // V^T row pitch (bytes)
+  static constexpr int KS = D * 2 + 16;         // K tile row pitch (bytes)
+  static constexpr int K_BYTES = BN * KS;
+  static constexpr int V_BYTES = D * VTP;     // V^T: one row per column d
+  static constexpr int LDS = 2 * K_BYTES + 2 * V_BYTES;  // two K stages, two V stages
+  static constexpr int CPR = D / 8;             // 16-byte chunks per K row
+  static constexpr int K_SLOTS = CPR + 1;       // ... plus one pad slot
+  static constexpr int K_LOADS = BN * K_SLOTS / 64;  // wave-wide 1 KiB direct loads per tile
+  static constexpr int KG = BN / 4;           // 4-key groups per tile
+  static constexpr int V_THREADS = KG * (D / 8);  // key groups x D/8 column chunks
+  static_assert(K_LOADS * 64 == BN * K_SLOTS, "K tile must be whole 1 KiB loads");
+  static_assert(V_THREADS <= THREADS, "V staging needs at most one thread per 4x8 block");
 };
-
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 __device__ inline bf16x8 pack_bf16(const float* x) {
   typedef float f32x8 __attribute__((ext_vector_type(8)));
@@ -45,9 +59,9 @@ __device__ inline bf16x8 pack_bf16(const float* x) {
   return __builtin_convertvector(v, bf16x8);
 }
 
-template <int D, bool CAUSAL, int EPI>
-__global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(FwdParams p) {
-  using G = Geo<D>;
+template <int D, bool CAUSAL, int EPI, int W, int BN>
+__global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
+  using G = Geo<D, W, BN>;
   __shared__ __attribute__((aligned(16))) char smem[G::LDS];
 
   const int tid = threadIdx.x;
@@ -58,7 +72,7 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(FwdParams p) {
 
   int qb, bh;
   map_block(blockIdx.x, p.nqb, p.BH, CAUSAL, qb, bh);
-  const int q0 = qb * kBM;
+  const int q0 = qb * G::BM;
   const int qw0 = q0 + wave * 32;
   const int my_q = qw0 + r32;
   const int Nq = p.Nq, Nk = p.Nk;
@@ -71,13 +85,13 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(FwdParams p) {
   // or beyond kend are skipped wholesale.
   int kend = Nk, wkend = Nk, wmask_from = Nk;
   if (CAUSAL) {
-    const int last_row = min(q0 + kBM, Nq) - 1;
+    const int last_row = min(q0 + G::BM, Nq) - 1;
     kend = min(Nk, last_row + p.diag + 1);
     wkend = min(Nk, min(qw0 + 31, Nq - 1) + p.diag + 1);
     wmask_from = min(Nk, qw0 + p.diag + 1);  // first key hidden from row qw0
   }
-  const int ntiles = kend > 0 ? (kend + kBN - 1) / kBN : 0;
-  const bool wave_live = qw0 < Nq;
+  const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+  const int wtiles = (qw0 < Nq && wkend > 0) ? min(ntiles, (wkend + BN - 1) / BN) : 0;
 
   // Q fragment (B operand of S^T = K Q^T): row my_q, d = kk*16 + g*8 .. +8.
   bf16x8 qf[D / 16];
@@ -87,153 +101,165 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       u32x4 x = ok ? src[kk * 2] : (u32x4){0u, 0u, 0u, 0u};
-      x ^= p.q_sign;
+      x = (x & p.q_and) ^ p.q_xor;
       qf[kk] = __builtin_bit_cast(bf16x8, x);
     }
   }
 
-  // Global -> register -> LDS staging of one K/V tile.
-  u32x4 kreg[G::PER_THREAD], vreg[G::PER_THREAD];
-  auto gload = [&](int t) {
-    const int k0 = t * kBN;
-#pragma unroll
-    for (int u = 0; u < G::PER_THREAD; ++u) {
-      const int ch = u * kThreads + tid;
-      const int row = ch / G::CPR, col = ch % G::CPR;
-      const int key = k0 + row;
-      if (key < Nk) {
-        kreg[u] = *(const u32x4*)(kg + (int64_t)key * D + col * 8);
-        vreg[u] = *(const u32x4*)(vg + (int64_t)key * D + col * 8);
-      } else {
-        kreg[u] = (u32x4){0u, 0u, 0u, 0u};
-        vreg[u] = (u32x4){0u, 0u, 0u, 0u};
-      }
+  // ---- staging.  K: direct global -> LDS loads; each wave-wide load fills 64
+  // consecutive 16-byte slots of the padded tile (slot s = row s / K_SLOTS,
+  // chunk s % K_SLOTS; the pad chunk re-reads chunk 0).  Keys past Nk read the
+  // last row: such tiles are always masked.  V: through registers, thread
+  // (dc, kgrp) takes keys 4*kgrp .. +3 of columns 8*dc .. +7 and stores them
+  // transposed (common.h).
+  const int v_dc = tid / G::KG, v_kg = tid % G::KG;
+  const bool v_stager = tid < G::V_THREADS;
+  u32x4 vreg[4];
+  auto kstage = [&](int t) { return smem + (t & 1) * G::K_BYTES; };
+  auto vstage = [&](int t) { return smem + 2 * G::K_BYTES + (t & 1) * G::V_BYTES; };
+  auto load_k = [&](int t) {
+    char* kb = kstage(t);
+    const int k0 = t * BN;
+    for (int j = wave; j < G::K_LOADS; j += W) {
+      const int slot = j * 64 + lane;
+      const int row = slot / G::K_SLOTS, ch = slot % G::K_SLOTS;
+      const int key = min(k0 + row, Nk - 1);
+      const uint16_t* src = kg + (int64_t)key * D + (ch < G::CPR ? ch : 0) * 8;
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(kb + j * 1024), 16, 0, 0);
     }
   };
-  auto lstore = [&](int stage) {
-    char* kb = smem + stage * G::STAGE;
-    char* vb = kb + G::K_BYTES;
+  auto gload_v = [&](int t) {
+    if (!v_stager) return;
+    const int k0 = t * BN;
 #pragma unroll
-    for (int u = 0; u < G::PER_THREAD; ++u) {
-      const int ch = u * kThreads + tid;
-      const int row = ch / G::CPR, col = ch % G::CPR;
-      *(u32x4*)(kb + row * G::KS + col * 16) = kreg[u];
-      *(u32x4*)(vb + row * G::VS + col * 16) = vreg[u];
+    for (int r = 0; r < 4; ++r) {
+      const int key = k0 + 4 * v_kg + r;
+      vreg[r] = key < Nk ? *(const u32x4*)(vg + (int64_t)key * D + v_dc * 8) : (u32x4){0u, 0u, 0u, 0u};
     }
+  };
+  auto lstore_v = [&](int t) {
+    if (v_stager) store_vt(vstage(t), G::VTP, 8 * v_dc, v_kg, vreg);
+  };
+  // Direct loads are counted by vmcnt only: drain them before the barrier that
+  // publishes the stage.
+  auto publish = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   };
 
+  // ---- per-row state
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = (f32x16){};
-  float m_raw = -INFINITY;  // running max of the raw dot product q.k
-  float l_lane = 0.f;       // this lane's share of the running normaliser
+  float m_run = -INFINITY;  // running maximum of the raw dot product q.k
+  float l_lane = 0.f;       // this lane's share of sum exp2(c (s - m_run))
   const float c = p.c;
 
-  // Per-lane LDS byte offsets. K: row r32, 16-byte slice g.  V (transposed
-  // read): source lane s = lane%16 addresses key 4g + s/4, columns
-  // 16*((lane/16)%2) + 4*(s%4) .. +4, so result lane r of each 16-lane group
-  // receives 4 consecutive keys of column r.
-  const int k_off = r32 * G::KS + g * 16;
-  const int s16 = lane & 15;
-  const int v_off = (4 * g + (s16 >> 2)) * G::VS + (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
+  const int k_off = r32 * G::KS + g * 16;     // K row r32, 16-byte slice g
+  const int v_off = r32 * G::VTP + g * 16;   // V^T row r32 of a 32-column block, slot 8g
 
-  if (ntiles > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int stage = t & 1;
-    const bool more = t + 1 < ntiles;
-    if (more) gload(t + 1);
-    const int k0 = t * kBN;
-    if (wave_live && k0 < wkend) {
-      const char* kb = smem + stage * G::STAGE;
-      const char* vb = kb + G::K_BYTES;
-
-      // S^T for two 32-key blocks h.
-      f32x16 s[2];
-      s[0] = (f32x16){};
-      s[1] = (f32x16){};
+  auto qk = [&](const char* kb, f32x16 (&s)[G::KB]) {
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
+    for (int h = 0; h < G::KB; ++h) s[h] = (f32x16){};
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const bf16x8 a = *(const bf16x8*)(kb + k_off + h * 32 * G::KS + kk * 32);
-          s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[h], 0, 0, 0);
-        }
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int h = 0; h < G::KB; ++h) {
+        const bf16x8 a = *(const bf16x8*)(kb + k_off + h * 32 * G::KS + kk * 32);
+        s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[h], 0, 0, 0);
       }
-
-      // Mask keys beyond the causal limit or the end of K (diagonal / tail
-      // tiles only).
-      const bool need_mask = k0 + kBN > wmask_from;
-      if (need_mask) {
-        const int lim = CAUSAL ? min(my_q + p.diag, Nk - 1) : Nk - 1;
+  };
+  // Keys beyond the causal limit or the end of K; exp2(-inf * c) = 0 as c > 0.
+  auto mask = [&](f32x16 (&s)[G::KB], int k0) {
+    const int lim = CAUSAL ? min(my_q + p.diag, Nk - 1) : Nk - 1;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < G::KB; ++h)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + 32 * h + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (key > lim) s[h][i] = -INFINITY;
-          }
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + 32 * h + 8 * (i >> 2) + 4 * g + (i & 3);
+        if (key > lim) s[h][i] = -INFINITY;
       }
-
-      // Online softmax update (base-2 exponent, scale folded into one FMA).
-      float mx = s[0][0];
+  };
+  auto tile_needs_mask = [&](int t) { return t * BN + BN > wmask_from; };
+  auto rowmax = [&](const f32x16 (&s)[G::KB]) {
+    float mx = s[0][0];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < G::KB; ++h)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[h][i]);
-      mx = halves_max(mx);
-      const float m_new = fmaxf(m_raw, mx);
-      const float alpha = (m_raw == -INFINITY) ? 0.f : fast_exp2((m_raw - m_new) * c);
-      const float bias = (m_new == -INFINITY) ? 0.f : -m_new * c;
-      float rs = 0.f;
-      bf16x8 pb[2][2];
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[h][i]);
+    return halves_max(mx);
+  };
+  // Raise the running maximum; where some row raised it, rescale O and l by
+  // alpha = exp2(c (m_old - m_new)).
+  auto rebase = [&](float mx) {
+    const bool need = mx > m_run;
+    if (__ballot(need)) {
+      const float m_new = need ? mx : m_run;
+      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_new) * c);
+      l_lane *= alpha;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          float pv[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float x = s[h][half * 8 + j];
-            float e = fast_exp2(fmaf(x, c, bias));
-            if (need_mask && x == -INFINITY) e = 0.f;
-            pv[j] = e;
-            rs += e;
-          }
-          pb[h][half] = pack_bf16(pv);
-        }
-      l_lane = alpha * l_lane + rs;
-      m_raw = m_new;
-      if (__ballot(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-      }
-
-      // O^T += V^T P^T.
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int key_off = (32 * h + 16 * half) * G::VS;
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            const char* base = vb + v_off + key_off + db * 64;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8 * G::VS));
-            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[h][half], oacc[db], 0, 0, 0);
-          }
-        }
+      for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+      m_run = m_new;
     }
-    if (more) lstore(stage ^ 1);
-    __syncthreads();
+  };
+  auto softmax = [&](const f32x16 (&s)[G::KB], bf16x8 (&pb)[G::KB][2]) {
+    const float bias = (m_run == -INFINITY) ? 0.f : -m_run * c;
+    float rs = 0.f;
+#pragma unroll
+    for (int h = 0; h < G::KB; ++h)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        float pv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          pv[j] = fast_exp2(fmaf(s[h][half * 8 + j], c, bias));
+          rs += pv[j];
+        }
+        pb[h][half] = pack_bf16(pv);
+      }
+    l_lane += rs;
+  };
+  auto pv_mma = [&](const char* vb, const bf16x8 (&pb)[G::KB][2]) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int h = 0; h < G::KB; ++h)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const bf16x8 a = *(const bf16x8*)(vb + v_off + db * 32 * G::VTP + (32 * h + 16 * half) * 2);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[h][half], oacc[db], 0, 0, 0);
+        }
+  };
+
+  // ---- tile loop: stage t%2 holds K(t) and V(t); tile t+1 is in flight
+  // while tile t is computed.
+  if (ntiles > 0) {
+    load_k(0);
+    gload_v(0);
+    lstore_v(0);
+  }
+  publish();
+  for (int t = 0; t < ntiles; ++t) {
+    const bool more = t + 1 < ntiles;
+    if (more) {
+      load_k(t + 1);
+      gload_v(t + 1);
+    }
+    if (t < wtiles) {
+      f32x16 sc[G::KB];
+      qk(kstage(t), sc);
+      if (tile_needs_mask(t)) mask(sc, t * BN);
+      rebase(rowmax(sc));
+      bf16x8 pb[G::KB][2];
+      softmax(sc, pb);
+      pv_mma(vstage(t), pb);
+    }
+    if (more) lstore_v(t + 1);
+    publish();
   }
 
-  // Epilogue: one division by the normaliser, one write of O.
+  // ---- epilogue: one division by the normaliser, one write of O.
   const float l_tot = halves_sum(l_lane);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (my_q < Nq) {
@@ -249,7 +275,7 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(FwdParams p) {
           *(bf16x4*)(og + 32 * db + 8 * r + 4 * g) = __builtin_convertvector(v, bf16x4);
         }
       if (p.lse && g == 0)
-        p.lse[row] = l_tot > 0.f ? m_raw * p.scale_abs + __log2f(l_tot) * 0.69314718055994530942f : -INFINITY;
+        p.lse[row] = l_tot > 0.f ? m_run * p.scale_abs + __log2f(l_tot) * 0.69314718055994530942f : -INFINITY;
     } else {
       float* og = (float*)p.o + row * D;
 #pragma unroll
@@ -262,10 +288,10 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(FwdParams p) {
         }
       if (g == 0) {
         if (EPI == kEpiState) {
-          p.m_out[row] = l_tot > 0.f ? m_raw * p.scale_abs : -INFINITY;
+          p.m_out[row] = l_tot > 0.f ? m_run * p.scale_abs : -INFINITY;
           p.l_out[row] = l_tot;
         } else if (p.lse) {
-          p.lse[row] = l_tot > 0.f ? m_raw * p.scale_abs + __log2f(l_tot) * 0.69314718055994530942f : -INFINITY;
+          p.lse[row] = l_tot > 0.f ? m_run * p.scale_abs + __log2f(l_tot) * 0.69314718055994530942f : -INFINITY;
         }
       }
     }
@@ -273,9 +299,11 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(FwdParams p) {
 }
 
 template <int D, bool CAUSAL, int EPI>
-static hipError_t launch_one(const FwdParams& p, hipStream_t s) {
+static hipError_t launch_one(FwdParams p, hipStream_t s) {
+  constexpr int W = kWavesBf16, BN = kTileBf16;
+  p.nqb = (p.Nq + 32 * W - 1) / (32 * W);
   const dim3 grid((unsigned)(p.nqb * p.BH));
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, EPI>), grid, dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, EPI, W, BN>), grid, dim3(64 * W), 0, s, p);
   return hipGetLastError();
 }
 

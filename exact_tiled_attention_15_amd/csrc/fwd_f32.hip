@@ -46,7 +46,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_f32_kernel(FwdParams p, int c
   }
   const int ntiles = kend > 0 ? (kend + kBN32 - 1) / kBN32 : 0;
   const bool wave_live = qw0 < Nq;
-  const float qsgn = p.q_sign ? -1.f : 1.f;
+  const float qsgn = p.q_and == 0u ? 0.f : (p.q_xor ? -1.f : 1.f);
 
   // Q fragment: B operand, row my_q, element kk holds d = 2*kk + g.
   float qf[D / 2];
@@ -100,8 +100,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_f32_kernel(FwdParams p, int c
       float rs = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float e = fast_exp2(fmaf(s[i], c, bias));
-        if (need_mask && s[i] == -INFINITY) e = 0.f;
+        const float e = fast_exp2(fmaf(s[i], c, bias));  // masked: exp2(-inf) = 0 as c > 0
         pr[i] = e;
         rs += e;
       }

@@ -31,17 +31,17 @@ namespace eta {
 template <int D, bool QK16>
 struct Geo8 {
   static constexpr int KS = QK16 ? 2 * D + 16 : D + 16;  // K tile row pitch (bytes)
-  static constexpr int VS = D * 2 + 64;     // V fp16 tile row pitch (bytes)
   static constexpr int K_BYTES = kBN * KS;
-  static constexpr int V_BYTES = kBN * VS;
+  static constexpr int V_BYTES = D * kVtPitch;  // fp16 V^T: one row per column d
   static constexpr int STAGE = K_BYTES + V_BYTES;
   static constexpr int LDS = 2 * STAGE;
   static constexpr int CPR = D / 16;        // 16-byte code chunks per row
   static constexpr int PER_THREAD = kBN * CPR / kThreads;
+  static constexpr int V_THREADS = 16 * (D / 8);  // 16 key groups x D/8 column chunks
   static_assert(PER_THREAD >= 1 && PER_THREAD * kThreads == kBN * CPR, "tile must split evenly");
+  static_assert(V_THREADS <= kThreads, "V staging needs at most one thread per 4x8 block");
 };
 
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4_8;
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 __device__ inline u32x4 widen_lo(const u32x4 w) {  // codes 0..7 of 16 -> fp16
@@ -112,13 +112,14 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_fp8_kernel(FwdParams p) {
   f16x8 qf16[QK16 ? QF : 1];
   {
     const bool ok = my_q < Nq;
-    const uint32_t sgn = p.q_sign ? 0x80808080u : 0u;
+    const uint32_t q_and = p.q_and ? 0xFFFFFFFFu : 0u;
+    const uint32_t sgn = p.q_xor ? 0x80808080u : 0u;
     const uint8_t* row = qg + (int64_t)(ok ? my_q : 0) * D;
     if constexpr (QK16) {
 #pragma unroll
       for (int kk = 0; kk < QF; ++kk) {
         u32x2 c = ok ? *(const u32x2*)(row + 16 * kk + 8 * g) : (u32x2){0u, 0u};
-        c ^= sgn;
+        c = (c & q_and) ^ sgn;
         const u32x4 w = {c[0], c[1], 0u, 0u};
         qf16[kk] = __builtin_bit_cast(f16x8, widen_lo(w));
       }
@@ -128,14 +129,20 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_fp8_kernel(FwdParams p) {
       for (int kk = 0; kk < QF; ++kk) {
         u32x4 a = ok ? src[kk * 4] : (u32x4){0u, 0u, 0u, 0u};
         u32x4 b = ok ? src[kk * 4 + 1] : (u32x4){0u, 0u, 0u, 0u};
-        a ^= sgn;
-        b ^= sgn;
+        a = (a & q_and) ^ sgn;
+        b = (b & q_and) ^ sgn;
         qf8[kk] = (i32x8){(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
       }
     }
   }
 
-  u32x4 kreg[G::PER_THREAD], vreg[G::PER_THREAD];
+  // K: 16-byte code chunks of rows.  V: thread (dc, kgrp) takes keys
+  // 4*kgrp .. +3 of columns 8*dc .. +7 (8 codes each), widens them to fp16 and
+  // stores them transposed (common.h).
+  const int v_dc = tid >> 4, v_kg = tid & 15;
+  const bool v_stager = tid < G::V_THREADS;
+  u32x4 kreg[G::PER_THREAD];
+  u32x2 vreg[4];
   auto gload = [&](int t) {
     const int k0 = t * kBN;
 #pragma unroll
@@ -143,20 +150,18 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_fp8_kernel(FwdParams p) {
       const int ch = u * kThreads + tid;
       const int row = ch / G::CPR, col = ch % G::CPR;
       const int key = k0 + row;
-      if (key < Nk) {
-        kreg[u] = *(const u32x4*)(kg + (int64_t)key * D + col * 16);
-        vreg[u] = *(const u32x4*)(vg + (int64_t)key * D + col * 16);
-      } else {
-        kreg[u] = (u32x4){0u, 0u, 0u, 0u};
-        vreg[u] = (u32x4){0u, 0u, 0u, 0u};
+      kreg[u] = key < Nk ? *(const u32x4*)(kg + (int64_t)key * D + col * 16) : (u32x4){0u, 0u, 0u, 0u};
+    }
+    if (v_stager) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = k0 + 4 * v_kg + r;
+        vreg[r] = key < Nk ? *(const u32x2*)(vg + (int64_t)key * D + v_dc * 8) : (u32x2){0u, 0u};
       }
     }
   };
-  // V codes are widened to fp16 (exact); K codes are stored as they are,
-  // or widened too in the fp16 form.
   auto lstore = [&](int stage) {
     char* kb = smem + stage * G::STAGE;
-    char* vb = kb + G::K_BYTES;
 #pragma unroll
     for (int u = 0; u < G::PER_THREAD; ++u) {
       const int ch = u * kThreads + tid;
@@ -167,8 +172,12 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_fp8_kernel(FwdParams p) {
       } else {
         *(u32x4*)(kb + row * G::KS + col * 16) = kreg[u];
       }
-      *(u32x4*)(vb + row * G::VS + col * 32) = widen_lo(vreg[u]);
-      *(u32x4*)(vb + row * G::VS + col * 32 + 16) = widen_hi(vreg[u]);
+    }
+    if (v_stager) {
+      u32x4 w[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[r] = widen_lo((u32x4){vreg[r][0], vreg[r][1], 0u, 0u});
+      store_vt(kb + G::K_BYTES, kVtPitch, 8 * v_dc, v_kg, w);
     }
   };
 
@@ -179,8 +188,7 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_fp8_kernel(FwdParams p) {
   float l_lane = 0.f;
 
   const int k_off = r32 * G::KS + g * (QK16 ? 16 : 32);
-  const int s16 = lane & 15;
-  const int v_off = (4 * g + (s16 >> 2)) * G::VS + (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
+  const int v_off = r32 * kVtPitch + g * 16;
 
   if (ntiles > 0) {
     gload(0);
@@ -204,6 +212,7 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_fp8_kernel(FwdParams p) {
       f32x16 s[2];
       s[0] = (f32x16){};
       s[1] = (f32x16){};
+      __builtin_amdgcn_s_setprio(1);
       if constexpr (QK16) {
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
@@ -227,6 +236,7 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_fp8_kernel(FwdParams p) {
           }
         }
       }
+      __builtin_amdgcn_s_setprio(0);
 
       const bool need_mask = k0 + kBN > wmask_from;
       if (need_mask) {
@@ -263,8 +273,7 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_fp8_kernel(FwdParams p) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const float x = s[h][half * 8 + j];
-            float e = fast_exp2(fmaf(x, c, bias_v));
-            if (need_mask && x == -INFINITY) e = 0.f;
+            const float e = fast_exp2(fmaf(x, c, bias_v));  // masked: exp2(-inf) = 0 as c > 0
             pv[j] = e;
             rs += e;
           }
@@ -278,20 +287,17 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_fp8_kernel(FwdParams p) {
         for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
       }
 
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int key_off = (32 * h + 16 * half) * G::VS;
+        for (int half = 0; half < 2; ++half)
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            const char* base = vb + v_off + key_off + db * 64;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_8*)(base));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_8*)(base + 8 * G::VS));
-            const f16x8 a = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            const f16x8 a = *(const f16x8*)(vb + v_off + db * 32 * kVtPitch + (32 * h + 16 * half) * 2);
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[h][half], oacc[db], 0, 0, 0);
           }
-        }
+      __builtin_amdgcn_s_setprio(0);
     }
     if (more) lstore(stage ^ 1);
     __syncthreads();
