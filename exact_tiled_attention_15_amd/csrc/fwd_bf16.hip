@@ -169,6 +169,15 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
         const bf16x8 a = *(const bf16x8*)(kb + k_off + h * 32 * G::KS + kk * 32);
         s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[h], 0, 0, 0);
       }
+    // LDS reads run 4 fragments ahead of the MFMAs (the default schedule
+    // waits for each fragment right before its MFMA)
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < G::KB * (D / 16) - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
   // Keys beyond the causal limit or the end of K; exp2(-inf * c) = 0 as c > 0.
   auto mask = [&](f32x16 (&s)[G::KB], int k0) {
@@ -230,6 +239,13 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
           const bf16x8 a = *(const bf16x8*)(vb + v_off + db * 32 * G::VTP + (32 * h + 16 * half) * 2);
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[h][half], oacc[db], 0, 0, 0);
         }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < (D / 32) * G::KB * 2 - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
 
   // ---- tile loop: stage t%2 holds K(t) and V(t); tile t+1 is in flight
