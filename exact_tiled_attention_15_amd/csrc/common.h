@@ -67,6 +67,19 @@ struct FwdParams {
 };
 
 // Launchers (host side). Each returns hipGetLastError() after the launch.
+// Compute units of the current device, cached per device (0 when unknown).
+inline int compute_units() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, int epi, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, bool qk16, hipStream_t s);
@@ -119,6 +132,17 @@ __device__ inline float halves_sum(float x) {
 }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// One wave-wide direct load of 64 x 16 bytes from global memory into LDS at
+// lds_base + 16 * lane.  Issued as assembly so the compiler does not treat
+// every later LDS read as possibly aliasing an outstanding transfer (which
+// makes it wait for all LDS reads before each use, defeating the read-ahead);
+// the kernel orders these transfers itself: vmcnt(0) and a barrier before any
+// wavefront reads the stage, and a barrier after the last read before the
+// stage is reloaded.
+__device__ inline void load_lds16(const void* src, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(src) : "memory", "m0");
+}
 
 // ---------------------------------------------------------------- V^T tile
 // The P.V product reads V with keys along the MFMA k dimension, i.e. 8 keys of

@@ -20,6 +20,12 @@
 // operand without any data movement.  The V^T fragments are single 16-byte
 // LDS reads from the transposed, key-permuted V tile (common.h).
 //
+// Issue order.  The probabilities of each 32-key block are formed right
+// before that block's P.V products, so the exponentials of the next block
+// issue between the current block's MFMAs: on gfx950 vector and matrix
+// instructions overlap when they are interleaved in one wavefront's
+// instruction stream.
+//
 // Staging.  A workgroup of W wavefronts owns 32*W query rows (W = 8: one
 // workgroup per compute unit, two wavefronts per SIMD), so every K/V tile read
 // from memory serves 256 rows.  K tiles go straight from global memory into LDS
@@ -125,8 +131,8 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
       const int row = slot / G::K_SLOTS, ch = slot % G::K_SLOTS;
       const int key = min(k0 + row, Nk - 1);
       const uint16_t* src = kg + (int64_t)key * D + (ch < G::CPR ? ch : 0) * 8;
-      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(kb + j * 1024), 16, 0, 0);
+      const unsigned base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)(kb + j * 1024);
+      load_lds16(src, __builtin_amdgcn_readfirstlane(base));
     }
   };
   auto gload_v = [&](int t) {
@@ -212,40 +218,46 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
       m_run = m_new;
     }
   };
-  auto softmax = [&](const f32x16 (&s)[G::KB], bf16x8 (&pb)[G::KB][2]) {
+  // P = exp2(c s - c m) (bf16) and O^T += V^T P^T, one 32-key block h at a
+  // time: block h's eight MFMAs need only block h's probabilities, so the
+  // exponentials of block h+1 issue between them (the scheduling pattern
+  // below asks for that order).  The row sum runs in four partial sums.
+  auto softmax_pv = [&](const f32x16 (&s)[G::KB], const char* vb) {
     const float bias = (m_run == -INFINITY) ? 0.f : -m_run * c;
-    float rs = 0.f;
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int h = 0; h < G::KB; ++h)
+    for (int h = 0; h < G::KB; ++h) {
+      bf16x8 pb[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         float pv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           pv[j] = fast_exp2(fmaf(s[h][half * 8 + j], c, bias));
-          rs += pv[j];
+          rs[j & 3] += pv[j];
         }
-        pb[h][half] = pack_bf16(pv);
+        pb[half] = pack_bf16(pv);
       }
-    l_lane += rs;
-  };
-  auto pv_mma = [&](const char* vb, const bf16x8 (&pb)[G::KB][2]) {
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int h = 0; h < G::KB; ++h)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const bf16x8 a = *(const bf16x8*)(vb + v_off + db * 32 * G::VTP + (32 * h + 16 * half) * 2);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[h][half], oacc[db], 0, 0, 0);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[half], oacc[db], 0, 0, 0);
         }
+    }
+    l_lane += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    constexpr int NM = (D / 32) * G::KB * 2;  // MFMAs
+    constexpr int VPB = 56;                   // vector instructions per block's probabilities
+    constexpr int VPM = (VPB + 2 * (D / 32) - 1) / (2 * (D / 32));  // per MFMA: one block's worth per block's MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x002, VPB, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int i = 0; i < (D / 32) * G::KB * 2 - 4; ++i) {
+    for (int i = 0; i < NM; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i + 4 < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
 
   // ---- tile loop: stage t%2 holds K(t) and V(t); tile t+1 is in flight
@@ -267,9 +279,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
       qk(kstage(t), sc);
       if (tile_needs_mask(t)) mask(sc, t * BN);
       rebase(rowmax(sc));
-      bf16x8 pb[G::KB][2];
-      softmax(sc, pb);
-      pv_mma(vstage(t), pb);
+      softmax_pv(sc, vstage(t));
     }
     if (more) lstore_v(t + 1);
     publish();

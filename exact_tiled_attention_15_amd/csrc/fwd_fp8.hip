@@ -174,8 +174,8 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
         const int row = slot / G::K_SLOTS, ch = slot % G::K_SLOTS;
         const int key = min(k0 + row, Nk - 1);
         const uint8_t* src = kg + (int64_t)key * D + (ch < G::CPR ? ch : 0) * 16;
-        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
-                                         (__attribute__((address_space(3))) void*)(kb + j * 1024), 16, 0, 0);
+        const unsigned base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)(kb + j * 1024);
+        load_lds16(src, __builtin_amdgcn_readfirstlane(base));
       }
     }
   };
