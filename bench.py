@@ -118,6 +118,21 @@ def main():
         step = lambda: eta.attn_fwd(q, k, v, o, lse, causal, scale, stream)
         kernel = "fwd_bf16_kernel"
         launches = 1
+    elif dtype == "bf16" and cfg.get("ring"):
+        nb = cfg["n_blocks"]
+        blk = Nk // nb
+        q, k, v = bf(x["q"]), bf(x["k"]), bf(x["v"])
+        kbs = [k[:, :, i * blk:(i + 1) * blk].contiguous() for i in range(nb)]
+        vbs = [v[:, :, i * blk:(i + 1) * blk].contiguous() for i in range(nb)]
+        del k, v
+        hops = configs.ring_hops(name)
+        kh, vh, pos = [kbs[b] for b, _ in hops], [vbs[b] for b, _ in hops], [kp for _, kp in hops]
+        o = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((B, H, Nq), device="cuda")
+        work = torch.empty((eta.ring_work_floats(B, H, Nq, d),), device="cuda")
+        step = lambda: eta.attn_fwd_ring(q, kh, vh, pos, o, lse, work, causal, cfg["q_pos0"], scale, stream)
+        kernel = "fwd_bf16_kernel (state epilogue) + merge_kernel, via attn_fwd_ring"
+        launches = 2 * nb - 1
     elif dtype == "bf16":
         nb = cfg["n_blocks"]
         blk = Nk // nb
@@ -155,7 +170,7 @@ def main():
         kernel = "fwd_fp8_kernel"
         launches = 1
 
-    flop = configs.flops(B, H, Nq, Nk, d, causal)
+    flop = configs.workload_flops(name)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

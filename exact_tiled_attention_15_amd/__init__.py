@@ -18,7 +18,9 @@ from ._lib import (  # noqa: F401
     attn_fwd_fp8,
     attn_fwd_fp8_qk16,
     attn_fwd_kvblock,
+    attn_fwd_ring,
     attn_merge,
     lib,
+    ring_work_floats,
     status_str,
 )

@@ -52,6 +52,10 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd_kvblock.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i64, i64, f, vp]
     L.attn_merge.restype = i
     L.attn_merge.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
+    L.attn_ring_work_floats.restype = ctypes.c_size_t
+    L.attn_ring_work_floats.argtypes = [i, i, i, i]
+    L.attn_fwd_ring.restype = i
+    L.attn_fwd_ring.argtypes = [vp, vp, vp, vp, i, vp, vp, vp, i, i, i, i, i, i, i64, f, vp]
     for name in ("attn_fwd_fp8", "attn_fwd_fp8_qk16"):
         fn = getattr(L, name)
         fn.restype = i
@@ -155,6 +159,36 @@ def attn_merge(o_acc, m_acc, l_acc, o_part, m_part, l_part, o_final=None, lse_fi
     _check(lib().attn_merge(_ptr(o_acc), _ptr(m_acc), _ptr(l_acc), _ptr(o_part), _ptr(m_part),
                             _ptr(l_part), _ptr(o_final), _ptr(lse_final), B, H, Nq, d,
                             _stream(stream)), "attn_merge")
+
+
+def ring_work_floats(B: int, H: int, Nq: int, d: int) -> int:
+    """Size (fp32 elements) of the workspace attn_fwd_ring needs."""
+    return int(lib().attn_ring_work_floats(B, H, Nq, d))
+
+
+def attn_fwd_ring(q, k_blks, v_blks, k_pos, o, lse, work, causal: bool, q_pos0: int, scale: float,
+                  stream=None):
+    """One GPU's ring-attention share: q bf16 [B,H,Nq,d] at global rows q_pos0.. against the
+    K/V blocks k_blks[b], v_blks[b] (bf16 [B,H,Nk_blk,d]) at global key positions k_pos[b]..,
+    in hop order; o bf16 [B,H,Nq,d], lse fp32 [B,H,Nq] or None, work fp32 of ring_work_floats."""
+    B, H, Nq, d = q.shape
+    n = len(k_blks)
+    if len(v_blks) != n or len(k_pos) != n:
+        raise ValueError("k_blks, v_blks and k_pos must have the same length")
+    Nkb = k_blks[0].shape[2] if n else 1
+    _want(q, torch.bfloat16, (B, H, Nq, d), "q")
+    for b in range(n):
+        _want(k_blks[b], torch.bfloat16, (B, H, Nkb, d), f"k_blks[{b}]")
+        _want(v_blks[b], torch.bfloat16, (B, H, Nkb, d), f"v_blks[{b}]")
+    _want(o, torch.bfloat16, (B, H, Nq, d), "o")
+    if lse is not None:
+        _want(lse, torch.float32, (B, H, Nq), "lse")
+    _want(work, torch.float32, (ring_work_floats(B, H, Nq, d),), "work")
+    kp = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in k_blks])
+    vp_ = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in v_blks])
+    pos = (ctypes.c_int64 * max(n, 1))(*[int(x) for x in k_pos])
+    _check(lib().attn_fwd_ring(_ptr(q), kp, vp_, pos, n, _ptr(o), _ptr(lse), _ptr(work), B, H, Nq, Nkb, d,
+                               int(bool(causal)), int(q_pos0), float(scale), _stream(stream)), "attn_fwd_ring")
 
 
 def _fwd_fp8(entry, q8, k8, v8, q_scale, k_scale, v_scale, o, lse, causal, scale, stream):

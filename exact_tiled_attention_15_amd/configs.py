@@ -21,6 +21,13 @@ WORKLOADS = {
     "bf16_kvblocks_B1_H16_Nq8192_Nk65536x8_d128": dict(index=3, B=1, H=16, Nq=8192, Nk=65536,
                                                        d=128, dtype="bf16", causal=False,
                                                        n_blocks=8, oracle_rows=512),
+    # One GPU's share of causal ring attention: the last of 8 ranks over a 65536-token
+    # sequence (contiguous sharding, the most loaded rank); its shard of 8192 query rows
+    # sits at global positions 57344.., and the ring delivers its own K/V block first,
+    # then its predecessors' (hop order 7, 6, .., 0).
+    "bf16_causal_ring_B1_H16_N65536_R8_d128": dict(index=5, B=1, H=16, Nq=8192, Nk=65536, d=128,
+                                                   dtype="bf16", causal=True, n_blocks=8,
+                                                   q_pos0=57344, ring=True, oracle_rows=256),
     # Block-quantized e4m3 with 1% outlier channels (x20), optional Hadamard rotation.
     "fp8_B4_H16_N4096_d128": dict(index=4, B=4, H=16, Nq=4096, Nk=4096, d=128, dtype="fp8",
                                   causal=False, outlier_frac=0.01, outlier_mult=20.0,
@@ -42,3 +49,24 @@ def flops(B: int, H: int, Nq: int, Nk: int, d: int, causal: bool) -> float:
     """Metric convention: 4*B*H*Nq*Nk*d, halved for a causal mask."""
     f = 4.0 * B * H * Nq * Nk * d
     return f / 2 if causal else f
+
+
+def ring_hops(name: str):
+    """(block index, global key position) per hop of a ring workload, in hop order."""
+    cfg = WORKLOADS[name]
+    nb, blk = cfg["n_blocks"], cfg["Nk"] // cfg["n_blocks"]
+    own = cfg["q_pos0"] // blk
+    order = [(own - h) % nb for h in range(nb)]
+    return [(b, b * blk) for b in order]
+
+
+def workload_flops(name: str) -> float:
+    """FLOPs credited to one pass of a workload: the metric convention, except that a
+    causal ring share counts its allowed (query, key) pairs exactly."""
+    cfg = WORKLOADS[name]
+    B, H, Nq, Nk, d = cfg["B"], cfg["H"], cfg["Nq"], cfg["Nk"], cfg["d"]
+    if cfg.get("ring") and cfg["causal"]:
+        q0 = cfg["q_pos0"]
+        pairs = Nq * q0 + Nq * (Nq + 1) // 2  # row q0 + i sees keys 0 .. q0 + i
+        return 4.0 * B * H * d * pairs
+    return flops(B, H, Nq, Nk, d, cfg["causal"])

@@ -68,6 +68,53 @@ FwdParams base_params(int B, int H, int Nq, int Nk, float scale) {
 
 attn_status from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
+// Partial (O, m, l) state of q against one K/V block at global positions
+// (arguments already validated).
+hipError_t launch_kvblock(const void* q, const void* k_blk, const void* v_blk, float* o_part, float* m_part,
+                          float* l_part, int B, int H, int Nq, int Nk_blk, int d, bool causal, int64_t q_pos0,
+                          int64_t k_pos0, float scale, hipStream_t stream) {
+  FwdParams p = base_params(B, H, Nq, Nk_blk, scale);
+  // Key j allowed for row i iff k_pos0 + j <= q_pos0 + i, i.e. j <= i + diag.
+  // Clamping diag to [-Nq, Nk] keeps every allowed set unchanged.
+  int64_t diag = q_pos0 - k_pos0;
+  if (diag > Nk_blk) diag = Nk_blk;
+  if (diag < -int64_t(Nq)) diag = -int64_t(Nq);
+  p.diag = int(diag);
+  p.q = q;
+  p.k = k_blk;
+  p.v = v_blk;
+  p.o = o_part;
+  p.m_out = m_part;
+  p.l_out = l_part;
+  return eta::launch_fwd_bf16(p, d, causal, eta::kEpiState, stream);
+}
+
+// Merge (o_part, m_part, l_part) into the accumulator (arguments already
+// validated).  Inside the library a null accumulator or part stands for the
+// empty state.
+hipError_t launch_merge_rows(float* o_acc, float* m_acc, float* l_acc, const float* o_part, const float* m_part,
+                             const float* l_part, void* o_final, float* lse_final, int64_t rows, int d,
+                             hipStream_t stream) {
+  eta::MergeParams p{};
+  p.o_acc = o_acc;
+  p.m_acc = m_acc;
+  p.l_acc = l_acc;
+  p.o_part = o_part;
+  p.m_part = m_part;
+  p.l_part = l_part;
+  p.o_final = o_final;
+  p.lse_final = lse_final;
+  p.rows = rows;
+  p.d = d;
+  return eta::launch_merge(p, stream);
+}
+
+bool merge_grid_ok(int64_t rows, int d) {
+  const int vpr = d / 4;
+  const int rpb = vpr >= 256 ? 1 : 256 / vpr;
+  return (rows + rpb - 1) / rpb <= INT32_MAX;
+}
+
 }  // namespace
 
 extern "C" {
@@ -122,20 +169,8 @@ attn_status attn_fwd_kvblock(const void* q, const void* k_blk, const void* v_blk
   if (attn_status s = check_ptrs4({m_part, l_part}, false)) return s;
   if (!std::isfinite(scale)) return ATTN_ERR_INVALID;
   if (causal && (q_pos0 < 0 || k_pos0 < 0)) return ATTN_ERR_INVALID;
-  FwdParams p = base_params(B, H, Nq, Nk_blk, scale);
-  // Key j allowed for row i iff k_pos0 + j <= q_pos0 + i, i.e. j <= i + diag.
-  // Clamping diag to [-Nq, Nk] keeps every allowed set unchanged.
-  int64_t diag = q_pos0 - k_pos0;
-  if (diag > Nk_blk) diag = Nk_blk;
-  if (diag < -int64_t(Nq)) diag = -int64_t(Nq);
-  p.diag = int(diag);
-  p.q = q;
-  p.k = k_blk;
-  p.v = v_blk;
-  p.o = o_part;
-  p.m_out = m_part;
-  p.l_out = l_part;
-  return from_hip(eta::launch_fwd_bf16(p, d, causal != 0, eta::kEpiState, (hipStream_t)stream));
+  return from_hip(launch_kvblock(q, k_blk, v_blk, o_part, m_part, l_part, B, H, Nq, Nk_blk, d, causal != 0,
+                                 q_pos0, k_pos0, scale, (hipStream_t)stream));
 }
 
 attn_status attn_merge(float* o_acc, float* m_acc, float* l_acc, const float* o_part,
@@ -148,22 +183,74 @@ attn_status attn_merge(float* o_acc, float* m_acc, float* l_acc, const float* o_
   if (attn_status s = check_ptrs4({lse_final}, true)) return s;
   if (o_final && !aligned(o_final, 8)) return ATTN_ERR_INVALID;
   const int64_t rows = int64_t(B) * H * Nq;
-  const int vpr = d / 4;
-  const int rpb = vpr >= 256 ? 1 : 256 / vpr;
-  if ((rows + rpb - 1) / rpb > INT32_MAX) return ATTN_ERR_INVALID;
+  if (!merge_grid_ok(rows, d)) return ATTN_ERR_INVALID;
   if (o_acc == o_part || m_acc == m_part || l_acc == l_part) return ATTN_ERR_INVALID;
-  eta::MergeParams p{};
-  p.o_acc = o_acc;
-  p.m_acc = m_acc;
-  p.l_acc = l_acc;
-  p.o_part = o_part;
-  p.m_part = m_part;
-  p.l_part = l_part;
-  p.o_final = o_final;
-  p.lse_final = lse_final;
-  p.rows = rows;
-  p.d = d;
-  return from_hip(eta::launch_merge(p, (hipStream_t)stream));
+  return from_hip(launch_merge_rows(o_acc, m_acc, l_acc, o_part, m_part, l_part, o_final, lse_final, rows, d,
+                                    (hipStream_t)stream));
+}
+
+size_t attn_ring_work_floats(int B, int H, int Nq, int d) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || d <= 0) return 0;
+  const size_t rows = size_t(B) * size_t(H) * size_t(Nq);
+  return 2 * rows * size_t(d) + 4 * rows;
+}
+
+attn_status attn_fwd_ring(const void* q, const void* const* k_blks, const void* const* v_blks,
+                          const int64_t* k_pos, int n_blk, void* o, float* lse, float* work, int B, int H,
+                          int Nq, int Nk_blk, int d, int causal, int64_t q_pos0, float scale, void* stream) {
+  if (n_blk < 0) return ATTN_ERR_INVALID;
+  if (attn_status s = check_shape(B, H, Nq, Nk_blk, d)) return s;
+  if (attn_status s = check_ptrs16({q, o, work})) return s;
+  if (attn_status s = check_ptrs4({lse}, true)) return s;
+  if (!std::isfinite(scale)) return ATTN_ERR_INVALID;
+  if (n_blk > 0 && (!k_blks || !v_blks || !k_pos)) return ATTN_ERR_INVALID;
+  if (causal && q_pos0 < 0) return ATTN_ERR_INVALID;
+  for (int b = 0; b < n_blk; ++b) {
+    if (attn_status s = check_ptrs16({k_blks[b], v_blks[b]})) return s;
+    if (causal && k_pos[b] < 0) return ATTN_ERR_INVALID;
+  }
+  const int64_t rows = int64_t(B) * H * Nq;
+  if (!merge_grid_ok(rows, d)) return ATTN_ERR_INVALID;
+  float* o_acc = work;
+  float* o_part = work + rows * d;
+  float* m_acc = work + 2 * rows * d;
+  float* l_acc = m_acc + rows;
+  float* m_part = l_acc + rows;
+  float* l_part = m_part + rows;
+  const hipStream_t s = (hipStream_t)stream;
+  // With a causal mask a block whose first key comes after the shard's last
+  // row holds no allowed key for any row: skip it.
+  const int64_t last_row = q_pos0 + Nq - 1;
+  auto live = [&](int b) { return !causal || k_pos[b] <= last_row; };
+  int n_live = 0, last_live = -1;
+  for (int b = 0; b < n_blk; ++b)
+    if (live(b)) {
+      ++n_live;
+      last_live = b;
+    }
+  if (n_live == 0)  // every row sees no key: O = 0, LSE = -inf
+    return from_hip(launch_merge_rows(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, o, lse, rows, d, s));
+  bool first = true;
+  for (int b = 0; b < n_blk; ++b) {
+    if (!live(b)) continue;
+    if (first) {  // the first live block's state becomes the accumulator
+      if (hipError_t e = launch_kvblock(q, k_blks[b], v_blks[b], o_acc, m_acc, l_acc, B, H, Nq, Nk_blk, d,
+                                        causal != 0, q_pos0, k_pos[b], scale, s))
+        return from_hip(e);
+      first = false;
+      continue;
+    }
+    if (hipError_t e = launch_kvblock(q, k_blks[b], v_blks[b], o_part, m_part, l_part, B, H, Nq, Nk_blk, d,
+                                      causal != 0, q_pos0, k_pos[b], scale, s))
+      return from_hip(e);
+    const bool last = b == last_live;
+    if (hipError_t e = launch_merge_rows(o_acc, m_acc, l_acc, o_part, m_part, l_part, last ? o : nullptr,
+                                         last ? lse : nullptr, rows, d, s))
+      return from_hip(e);
+  }
+  if (n_live == 1)  // finish the single block: merge it with the empty state
+    return from_hip(launch_merge_rows(o_acc, m_acc, l_acc, nullptr, nullptr, nullptr, o, lse, rows, d, s));
+  return ATTN_OK;
 }
 
 static attn_status fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,

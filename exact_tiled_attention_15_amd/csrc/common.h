@@ -67,19 +67,6 @@ struct FwdParams {
 };
 
 // Launchers (host side). Each returns hipGetLastError() after the launch.
-// Compute units of the current device, cached per device (0 when unknown).
-inline int compute_units() {
-  static int cache[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
-
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, int epi, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, bool qk16, hipStream_t s);

@@ -301,10 +301,13 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
       // P' = p * s_v(t) / s_v_max: the tile's V scale rides in the exponent
       // bias; the normaliser gets p back through one multiply per tile.
       const float bias_v = ((m2 == -INFINITY) ? 0.f : -m2) + vfold;
-      float rs = 0.f;
-      f16x8 pb[G::KB][2];
+      // P' = exp2(...) in fp16 and O^T += V^T P'^T, one 32-key block h at a
+      // time: block h's MFMAs need only block h's probabilities, so the
+      // exponentials of block h+1 issue between them.  Four partial sums.
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int h = 0; h < G::KB; ++h)
+      for (int h = 0; h < G::KB; ++h) {
+        f16x8 pb[2];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           f32x8 pv;
@@ -312,21 +315,32 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
           for (int j = 0; j < 8; ++j) {
             const float e = fast_exp2(fmaf(s[h][half * 8 + j], c, bias_v));  // masked: exp2(-inf) = 0
             pv[j] = e;
-            rs += e;
+            rs[j & 3] += e;
           }
-          pb[h][half] = __builtin_convertvector(pv, f16x8);
+          pb[half] = __builtin_convertvector(pv, f16x8);
         }
-      l_lane += rs * vunfold;
-
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int h = 0; h < G::KB; ++h)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
             const f16x8 a = *(const f16x8*)(vstage(t) + v_off + db * 32 * G::VTP + (32 * h + 16 * half) * 2);
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[h][half], oacc[db], 0, 0, 0);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[half], oacc[db], 0, 0, 0);
           }
+      }
+      l_lane += ((rs[0] + rs[1]) + (rs[2] + rs[3])) * vunfold;
+      {
+        constexpr int NM = (D / 32) * G::KB * 2;
+        constexpr int VPB = 56;  // vector instructions of one block's probabilities
+        constexpr int VPM = (VPB + 2 * (D / 32) - 1) / (2 * (D / 32));
+        __builtin_amdgcn_sched_group_barrier(0x002, VPB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i + 4 < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+        }
+      }
     }
     if (more) {
       store_k(t + 1);

@@ -18,9 +18,13 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeParams p, int vpr, int 
 
   float M = -INFINITY, l = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  // A null accumulator or part stands for the empty state (m = -inf, l = 0),
+  // the identity of the merge: the library's ring driver uses it to finish a
+  // single block (null part) or an all-masked shard (both null).
+  const bool has_acc = p.o_acc != nullptr, has_part = p.o_part != nullptr;
   if (live) {
-    const float ma = p.m_acc[row], mb = p.m_part[row];
-    const float la = p.l_acc[row], lb = p.l_part[row];
+    const float ma = has_acc ? p.m_acc[row] : -INFINITY, mb = has_part ? p.m_part[row] : -INFINITY;
+    const float la = has_acc ? p.l_acc[row] : 0.f, lb = has_part ? p.l_part[row] : 0.f;
     M = fmaxf(ma, mb);
     float wa = 0.f, wb = 0.f;
     if (M != -INFINITY) {
@@ -30,18 +34,21 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeParams p, int vpr, int 
     l = wa + wb;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int64_t off = row * p.d + 4 * cv;
-    const f32x4 oa = *(const f32x4*)(p.o_acc + off);
-    const f32x4 ob = *(const f32x4*)(p.o_part + off);
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 oa = wa > 0.f ? *(const f32x4*)(p.o_acc + off) : zero;
+    const f32x4 ob = wb > 0.f ? *(const f32x4*)(p.o_part + off) : zero;
     o = (wa * oa + wb * ob) * inv;
   }
   __syncthreads();  // every read of m_acc / l_acc of this block's rows is done
   if (!live) return;
   const int64_t off = row * p.d + 4 * cv;
-  *(f32x4*)(p.o_acc + off) = o;
+  if (has_acc) *(f32x4*)(p.o_acc + off) = o;
   if (p.o_final) *(bf16x4*)((uint16_t*)p.o_final + off) = __builtin_convertvector(o, bf16x4);
   if (cv == 0) {
-    p.m_acc[row] = l > 0.f ? M : -INFINITY;
-    p.l_acc[row] = l;
+    if (has_acc) {
+      p.m_acc[row] = l > 0.f ? M : -INFINITY;
+      p.l_acc[row] = l;
+    }
     if (p.lse_final) p.lse_final[row] = l > 0.f ? M + logf(l) : -INFINITY;
   }
 }

@@ -43,6 +43,7 @@
 #ifndef ATTN_H
 #define ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -131,6 +132,36 @@ attn_status attn_merge(float* o_acc, float* m_acc, float* l_acc,
                        const float* o_part, const float* m_part, const float* l_part,
                        void* o_final, float* lse_final,
                        int B, int H, int Nq, int d, void* stream);
+
+/*
+ * attn_fwd_ring - one GPU's whole share of ring attention ("Sequence
+ * parallelism and ring attention", "Deep dive" and "Technical insight"):
+ * the local query shard against the K/V blocks that the ring's hops deliver,
+ * in hop order, each block's partial state (as attn_fwd_kvblock) folded into
+ * a running state (as attn_merge), then the final bf16 O and LSE.
+ *   q       bf16 [B,H,Nq,d], query row i at global position q_pos0 + i
+ *   k_blks, v_blks   HOST arrays of n_blk device pointers, each block
+ *                    bf16 [B,H,Nk_blk,d]; block b's key j sits at global
+ *                    position k_pos[b] + j (k_pos: HOST array of n_blk)
+ *   o       bf16 [B,H,Nq,d]      lse  fp32 [B,H,Nq] natural log, or NULL
+ *   work    device fp32 workspace of attn_ring_work_floats(B,H,Nq,d)
+ *           floats, 16-byte aligned, owned by the caller; its contents on
+ *           return are unspecified.  It must not overlap any other argument.
+ * With `causal` set, key position kp is allowed for query position qp iff
+ * kp <= qp; a block whose first key lies after the shard's last row holds no
+ * allowed key and is skipped without a launch.  n_blk = 0, or every block
+ * skipped, gives O = 0 and LSE = -inf.  The blocks must already be resident
+ * on this device: the library moves no data between GPUs.
+ * Errors: as attn_fwd_kvblock, plus ATTN_ERR_INVALID for n_blk < 0, NULL
+ * arrays with n_blk > 0, a NULL or misaligned block, or a negative position
+ * with `causal` set.  Arguments are all checked before the first launch; a
+ * launch failure returns ATTN_ERR_HIP with the earlier steps enqueued.
+ */
+size_t attn_ring_work_floats(int B, int H, int Nq, int d);
+attn_status attn_fwd_ring(const void* q, const void* const* k_blks, const void* const* v_blks,
+                          const int64_t* k_pos, int n_blk, void* o, float* lse, float* work,
+                          int B, int H, int Nq, int Nk_blk, int d, int causal, int64_t q_pos0,
+                          float scale, void* stream);
 
 /*
  * attn_fwd_fp8 - attention on block-quantized OCP FP8 E4M3 ("e4m3fn") inputs

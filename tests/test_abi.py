@@ -95,3 +95,29 @@ def test_kvblock_and_merge_validation():
     assert mg(P16, P16) == eta.ATTN_ERR_INVALID            # o_acc aliases o_part
     assert mg(P16, P16b, ma=P4, mp=P4) == eta.ATTN_ERR_INVALID  # m_acc aliases m_part
     assert mg(P16, P16b, of=ctypes.c_void_p(0x50002)) == eta.ATTN_ERR_INVALID
+
+
+def test_ring_validation():
+    """attn_fwd_ring rejects bad arguments before any launch (fake pointers are never touched)."""
+    L = eta.lib()
+    assert L.attn_ring_work_floats(1, 2, 8, 64) == 2 * 16 * 64 + 4 * 16
+    assert L.attn_ring_work_floats(0, 2, 8, 64) == 0
+    ks = (ctypes.c_void_p * 2)(0x100000, 0x200000)
+    vs = (ctypes.c_void_p * 2)(0x300000, 0x400000)
+    pos = (ctypes.c_int64 * 2)(0, 8)
+    bad_pos = (ctypes.c_int64 * 2)(0, -8)
+    mis = (ctypes.c_void_p * 2)(0x100000, 0x200004)
+    nulls = (ctypes.c_void_p * 2)(0x100000, 0)
+    ring = lambda n=2, k=ks, v=vs, p=pos, q=P16, o=P16b, w=P16c, causal=1, qp=8, d=64, scale=0.1: L.attn_fwd_ring(
+        q, k, v, p, n, o, NUL, w, 1, 1, 8, 8, d, causal, qp, scale, None)
+    assert ring(n=-1) == eta.ATTN_ERR_INVALID
+    assert ring(k=None) == eta.ATTN_ERR_INVALID           # NULL arrays with blocks
+    assert ring(p=None) == eta.ATTN_ERR_INVALID
+    assert ring(p=bad_pos) == eta.ATTN_ERR_INVALID         # negative position, causal
+    assert ring(qp=-1) == eta.ATTN_ERR_INVALID
+    assert ring(k=mis) == eta.ATTN_ERR_INVALID             # misaligned block
+    assert ring(v=nulls) == eta.ATTN_ERR_INVALID           # NULL block
+    assert ring(w=NUL) == eta.ATTN_ERR_INVALID             # no workspace
+    assert ring(w=MIS) == eta.ATTN_ERR_INVALID             # misaligned workspace
+    assert ring(d=96) == eta.ATTN_ERR_UNSUPPORTED
+    assert ring(scale=float("nan")) == eta.ATTN_ERR_INVALID

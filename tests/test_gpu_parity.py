@@ -336,6 +336,71 @@ def test_workload_kv_blocks():
     compare_o(o_1[:, :, rows], ro, BF16_BAR, "one-pass vs oracle")
 
 
+# ------------------------------------------------------- ring-attention share
+def _ring_run(q, k_full, v_full, blk, order, causal, q_pos0, scale):
+    """attn_fwd_ring over the blocks of k_full / v_full (blk keys each) in the given hop order."""
+    B, H, Nq, d = q.shape
+    kb = [k_full[:, :, b * blk:(b + 1) * blk].contiguous() for b in order]
+    vb = [v_full[:, :, b * blk:(b + 1) * blk].contiguous() for b in order]
+    pos = [b * blk for b in order]
+    o = torch.full((B, H, Nq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, H, Nq), float("nan"), device="cuda")
+    work = torch.full((eta.ring_work_floats(B, H, Nq, d),), float("nan"), device="cuda")
+    eta.attn_fwd_ring(q, kb, vb, pos, o, lse, work, causal, q_pos0, scale)
+    torch.cuda.synchronize()
+    return host(o), host(lse)
+
+
+@pytest.mark.parametrize("N,blk,q_pos0,Nq,causal,order", [
+    (1000, 250, 500, 250, True, [2, 1, 0, 3]),     # diagonal block, two full ones, one skipped
+    (1000, 250, 0, 250, True, [0, 3, 2, 1]),       # one live block: finished against the empty state
+    (924, 77, 300, 130, True, list(range(12))),    # ragged: the diagonal falls inside blocks
+    (600, 200, 123, 200, False, [2, 0, 1]),        # no mask: every block, any order
+])
+def test_ring_share_matches_oracle(N, blk, q_pos0, Nq, causal, order):
+    say(f"ring N={N} blk={blk} q_pos0={q_pos0} Nq={Nq} causal={causal} order={order}")
+    qb, kb, vb = _bf16_problem(1, 2, N, N, 128, N + blk)
+    q_sh = qb[:, :, q_pos0:q_pos0 + Nq]
+    o, lse = _ring_run(dev_bf16(q_sh), dev_bf16(kb), dev_bf16(vb), blk, order, causal, q_pos0, 0.1)
+    # global causal rule for the shard = bottom-right alignment over keys [0, q_pos0 + Nq)
+    kend = q_pos0 + Nq if causal else N
+    ro, rl = oracle.attention(oracle.decode_bf16(q_sh), oracle.decode_bf16(kb[:, :, :kend]),
+                              oracle.decode_bf16(vb[:, :, :kend]), causal, 0.1)
+    compare_o(o, ro, BF16_BAR, "ring O")
+    compare_lse(lse, rl, "ring LSE")
+
+
+def test_ring_share_without_allowed_keys():
+    say("ring with every block masked, and with no block")
+    qb, kb, vb = _bf16_problem(1, 2, 300, 300, 64, 5)
+    q = dev_bf16(qb[:, :, :100])
+    for order in ([1, 2], []):  # blocks at keys 100.. and 200..: after every row of the shard
+        o, lse = _ring_run(q, dev_bf16(kb), dev_bf16(vb), 100, order, True, 0, 0.1)
+        assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+def test_workload_ring_share():
+    name = "bf16_causal_ring_B1_H16_N65536_R8_d128"
+    say(name)
+    cfg, seed = configs.WORKLOADS[name], configs.seed_of(name)
+    B, H, Nq, Nk, d, nb = cfg["B"], cfg["H"], cfg["Nq"], cfg["Nk"], cfg["d"], cfg["n_blocks"]
+    scale, q_pos0 = configs.scale_of(name), cfg["q_pos0"]
+    x = inputs.make_inputs(cfg, seed)
+    q, k, v = dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"])
+    order = [b for b, _ in configs.ring_hops(name)]
+    o_r, l_r = _ring_run(q, k, v, Nk // nb, order, True, q_pos0, scale)
+    # this shard ends at the last key, so one-pass causal attention over all keys is the same problem
+    assert q_pos0 + Nq == Nk
+    o_1, l_1 = _run_fwd(x["q"], x["k"], x["v"], True, scale)
+    compare_o(o_r, o_1, BF16_BAR, "ring vs one-pass (all rows)")
+    compare_lse(l_r, l_1, "ring vs one-pass LSE")
+    rows = _sample_rows(Nq, cfg["oracle_rows"], seed)
+    ro, rl = oracle.attention(oracle.decode_bf16(x["q"]), oracle.decode_bf16(x["k"]), oracle.decode_bf16(x["v"]),
+                              True, scale, rows=rows)
+    compare_o(o_r[:, :, rows], ro, BF16_BAR, "ring vs oracle")
+    compare_lse(l_r[:, :, rows], rl, "ring LSE vs oracle")
+
+
 @pytest.mark.parametrize("rotate,mode", [(False, "qk16"), (True, "fp8"), (True, "qk16"), (False, "fp8")])
 def test_workload_fp8(rotate, mode):
     name = "fp8_B4_H16_N4096_d128"

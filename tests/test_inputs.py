@@ -94,3 +94,20 @@ def test_row_subset_and_determinism():
 def test_flop_convention():
     assert configs.flops(8, 16, 2048, 2048, 128, True) == 4 * 8 * 16 * 2048 * 2048 * 128 / 2
     assert configs.flops(1, 16, 8192, 65536, 128, False) == 4 * 16 * 8192 * 65536 * 128
+
+
+def test_ring_workload_hops_and_flops():
+    """The ring workload visits every block once, its own block first, and credits exactly the
+    (query, key) pairs a global causal mask allows (counted row by row here)."""
+    name = "bf16_causal_ring_B1_H16_N65536_R8_d128"
+    cfg = configs.WORKLOADS[name]
+    hops = configs.ring_hops(name)
+    blk = cfg["Nk"] // cfg["n_blocks"]
+    assert sorted(b for b, _ in hops) == list(range(cfg["n_blocks"]))
+    assert hops[0][0] == cfg["q_pos0"] // blk
+    assert all(kp == b * blk for b, kp in hops)
+    rows = np.arange(cfg["q_pos0"], cfg["q_pos0"] + cfg["Nq"], dtype=np.int64)
+    allowed = np.minimum(rows + 1, cfg["Nk"]).sum()
+    assert configs.workload_flops(name) == 4.0 * cfg["B"] * cfg["H"] * cfg["d"] * float(allowed)
+    # the other workloads keep the metric convention
+    assert configs.workload_flops("bf16_causal_B8_H16_N2048_d128") == configs.flops(8, 16, 2048, 2048, 128, True)
