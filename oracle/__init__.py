@@ -54,6 +54,9 @@ def _L():
         L.oracle_state_lse.argtypes = [vp, vp, i64, vp]
         L.oracle_num_threads.restype = i
         L.oracle_num_threads.argtypes = []
+        L.oracle_attention_bwd.restype = i
+        L.oracle_attention_bwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i, d, vp, i64, vp, i64,
+                                           vp, vp, vp]
         _lib = L
     return _lib
 
@@ -155,3 +158,23 @@ def state_lse(m, l):
     out = np.empty_like(m)
     _L().oracle_state_lse(_p(m), _p(l), m.size, _p(out))
     return out
+
+
+def attention_bwd(q, k, v, dout, causal: bool, scale: float, q_rows=None, k_rows=None):
+    """fp64 gradients of sum(dout * O) for standard attention: dq for the query rows q_rows
+    ([B,H,n_q,d], all rows if None) and dk, dv for the key rows k_rows ([B,H,n_k,d])."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    qr = None if q_rows is None else np.ascontiguousarray(q_rows, dtype=np.int64)
+    kr = None if k_rows is None else np.ascontiguousarray(k_rows, dtype=np.int64)
+    RQ = Nq if qr is None else len(qr)
+    RK = Nk if kr is None else len(kr)
+    dq = np.empty((B, H, RQ, d))
+    dk = np.empty((B, H, RK, d))
+    dv = np.empty((B, H, RK, d))
+    rc = _L().oracle_attention_bwd(_p(q), _p(k), _p(v), _p(dout), B, H, Nq, Nk, d, int(bool(causal)),
+                                   float(scale), _p(qr), RQ, _p(kr), RK, _p(dq), _p(dk), _p(dv))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attention_bwd failed ({rc})")
+    return dq, dk, dv

@@ -38,6 +38,14 @@
  *    quantization" (itimpress), section 1, FP8 bullet.  Both decodes are exact in
  *    fp64.
  *
+ *  - The gradients of that attention (the backward pass that the training
+ *    results of "FlashAttention-2" ("Performance and efficiency") and of the
+ *    FlashAttention-4 summary presuppose; the pages give no formula, so this is
+ *    the chain rule applied to the definition above).  For one (b, h) and the
+ *    loss L = sum_i dO_i . O_i:  dV_j = sum_i P_ij dO_i ;
+ *    dP_ij = dO_i . v_j ;  D_i = sum_j P_ij dP_ij ;  dS_ij = P_ij (dP_ij - D_i) ;
+ *    dQ_i = scale sum_j dS_ij k_j ;  dK_j = scale sum_i dS_ij q_i.
+ *
  * Layout of every tensor: contiguous [B, H, N, d], d innermost; per-row outputs
  * [B, H, N].  A row subset is given as `rows` (n_rows query indices shared by
  * every (b, h)), or rows == NULL for all Nq rows; outputs are then
@@ -258,6 +266,118 @@ void oracle_merge(double* o_a, double* m_a, double* l_a,
 void oracle_state_lse(const double* m, const double* l, int64_t n, double* lse) {
     for (int64_t r = 0; r < n; ++r)
         lse[r] = (m[r] == -INFINITY || l[r] <= 0.0) ? -INFINITY : m[r] + log(l[r]);
+}
+
+/* ------------------------------------------------------------- gradients */
+
+/* Gradients of L = sum dO . O with respect to q, k and v (formulas in the
+ * header).  q, dout: [B,H,Nq,d]; k, v: [B,H,Nk,d].  dq gets the rows q_rows
+ * ([B,H,n_q,d]; all Nq rows when q_rows == NULL), dk and dv the key rows
+ * k_rows ([B,H,n_k,d]; all Nk rows when k_rows == NULL).  Each (b, h) first
+ * computes every query row's log-sum-exp and D_i, then the requested rows
+ * one by one, each as a sum over the other side's rows. */
+int oracle_attention_bwd(const double* q, const double* k, const double* v, const double* dout,
+                         int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                         int causal, double scale,
+                         const int64_t* q_rows, int64_t n_q, const int64_t* k_rows, int64_t n_k,
+                         double* dq, double* dk, double* dv) {
+    if (B <= 0 || H <= 0 || Nq < 0 || Nk < 0 || d <= 0) return -1;
+    const int64_t RQ = q_rows ? n_q : Nq, RK = k_rows ? n_k : Nk, BH = B * H;
+    double* lse = (double*)malloc(sizeof(double) * (size_t)(BH * Nq > 0 ? BH * Nq : 1));
+    double* Dr = (double*)malloc(sizeof(double) * (size_t)(BH * Nq > 0 ? BH * Nq : 1));
+    if (!lse || !Dr) {
+        free(lse);
+        free(Dr);
+        return -2;
+    }
+    int err = 0;
+    /* pass 1: per query row, the log-sum-exp and D_i = sum_j P_ij dP_ij */
+#pragma omp parallel
+    {
+        double* s_buf = (double*)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+        double* p_buf = (double*)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+        double* o_buf = (double*)malloc(sizeof(double) * (size_t)d);
+        if (!s_buf || !p_buf || !o_buf) {
+#pragma omp atomic write
+            err = -2;
+        }
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t u = 0; u < BH * Nq; ++u) {
+            if (!s_buf || !p_buf || !o_buf) continue;
+            const int64_t bh = u / Nq, i = u % Nq;
+            const int64_t count = causal ? prefix_count(i + Nk - Nq, Nk) : Nk;
+            const double* qi = q + (bh * Nq + i) * d;
+            const double* doi = dout + (bh * Nq + i) * d;
+            double m, l;
+            row_attention(qi, k + bh * Nk * d, v + bh * Nk * d, Nk, d, count, scale, s_buf, o_buf, &m, &l, p_buf);
+            lse[u] = count > 0 ? m + log(l) : -INFINITY;
+            double D = 0.0;
+            for (int64_t j = 0; j < count; ++j) {
+                double dp = 0.0;
+                for (int64_t c = 0; c < d; ++c) dp += doi[c] * v[(bh * Nk + j) * d + c];
+                D += p_buf[j] * dp;
+            }
+            Dr[u] = D;
+        }
+        free(s_buf);
+        free(p_buf);
+        free(o_buf);
+    }
+    if (err) {
+        free(lse);
+        free(Dr);
+        return err;
+    }
+    /* P_ij and dS_ij from the row statistics */
+#define ORACLE_P(bh, i, j, p_out, ds_out)                                                  \
+    do {                                                                                 \
+        const double* qi_ = q + ((bh) * Nq + (i)) * d;                                   \
+        const double* di_ = dout + ((bh) * Nq + (i)) * d;                                \
+        const double* kj_ = k + ((bh) * Nk + (j)) * d;                                   \
+        const double* vj_ = v + ((bh) * Nk + (j)) * d;                                   \
+        double dot_ = 0.0, dp_ = 0.0;                                                    \
+        for (int64_t c_ = 0; c_ < d; ++c_) {                                             \
+            dot_ += qi_[c_] * kj_[c_];                                                   \
+            dp_ += di_[c_] * vj_[c_];                                                    \
+        }                                                                                \
+        (p_out) = exp(scale * dot_ - lse[(bh) * Nq + (i)]);                              \
+        (ds_out) = (p_out) * (dp_ - Dr[(bh) * Nq + (i)]);                                \
+    } while (0)
+    /* pass 2: dq rows */
+#pragma omp parallel for schedule(dynamic, 8)
+    for (int64_t u = 0; u < BH * RQ; ++u) {
+        const int64_t bh = u / RQ, r = u % RQ, i = q_rows ? q_rows[r] : r;
+        double* out = dq + u * d;
+        for (int64_t c = 0; c < d; ++c) out[c] = 0.0;
+        const int64_t count = causal ? prefix_count(i + Nk - Nq, Nk) : Nk;
+        for (int64_t j = 0; j < count; ++j) {
+            double P, dS;
+            ORACLE_P(bh, i, j, P, dS);
+            (void)P;
+            for (int64_t c = 0; c < d; ++c) out[c] += scale * dS * k[(bh * Nk + j) * d + c];
+        }
+    }
+    /* pass 3: dk and dv rows; key j is seen by the rows i with j <= i + Nk - Nq */
+#pragma omp parallel for schedule(dynamic, 8)
+    for (int64_t u = 0; u < BH * RK; ++u) {
+        const int64_t bh = u / RK, r = u % RK, j = k_rows ? k_rows[r] : r;
+        double* gk = dk + u * d;
+        double* gv = dv + u * d;
+        for (int64_t c = 0; c < d; ++c) gk[c] = gv[c] = 0.0;
+        const int64_t i0 = causal ? (j - (Nk - Nq) > 0 ? j - (Nk - Nq) : 0) : 0;
+        for (int64_t i = i0; i < Nq; ++i) {
+            double P, dS;
+            ORACLE_P(bh, i, j, P, dS);
+            for (int64_t c = 0; c < d; ++c) {
+                gv[c] += P * dout[(bh * Nq + i) * d + c];
+                gk[c] += scale * dS * q[(bh * Nq + i) * d + c];
+            }
+        }
+    }
+#undef ORACLE_P
+    free(lse);
+    free(Dr);
+    return 0;
 }
 
 int oracle_num_threads(void) {

@@ -252,3 +252,70 @@ def test_e4m3_decode_applies_tile_scales():
     for h in range(2):
         for n in range(300):
             assert np.all(x[0, h, n] == scales[0, h, n // 128])
+
+
+# ------------------------------------------------------------------ gradients
+def _loss(q, k, v, dout, causal, scale):
+    o, _ = oracle.attention(q, k, v, causal, scale)
+    return float((o * dout).sum())
+
+
+@pytest.mark.parametrize("Nq,Nk,causal", [(5, 6, False), (5, 6, True), (6, 4, True), (3, 3, True)])
+def test_bwd_matches_finite_differences_of_the_forward(Nq, Nk, causal):
+    """Every gradient entry equals the central difference of sum(dO * O) computed with the
+    (separately pinned) forward oracle; Nq > Nk causal includes rows with no key."""
+    rng = np.random.default_rng(Nq * 10 + Nk + causal)
+    q, k, v, do = (rng.standard_normal(s) for s in [(1, 2, Nq, 4), (1, 2, Nk, 4), (1, 2, Nk, 4), (1, 2, Nq, 4)])
+    scale, h = 0.7, 1e-5
+    grads = dict(zip("qkv", oracle.attention_bwd(q, k, v, do, causal, scale)))
+    base = {"q": q, "k": k, "v": v}
+    for name in "qkv":
+        num = np.zeros_like(base[name])
+        for idx in np.ndindex(base[name].shape):
+            plus = {n: a.copy() for n, a in base.items()}
+            minus = {n: a.copy() for n, a in base.items()}
+            plus[name][idx] += h
+            minus[name][idx] -= h
+            num[idx] = (_loss(plus["q"], plus["k"], plus["v"], do, causal, scale)
+                        - _loss(minus["q"], minus["k"], minus["v"], do, causal, scale)) / (2 * h)
+        np.testing.assert_allclose(grads[name], num, atol=1e-8, rtol=0, err_msg=f"d{name}")
+
+
+def test_bwd_single_key_closed_form():
+    """One key: P = 1 for every row, so the output is v whatever q and k: dq = dk = 0, dv = sum_i dO_i."""
+    rng = np.random.default_rng(3)
+    q, do = rng.standard_normal((2, 1, 7, 8)), rng.standard_normal((2, 1, 7, 8))
+    k, v = rng.standard_normal((2, 1, 1, 8)), rng.standard_normal((2, 1, 1, 8))
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, False, 0.3)
+    assert np.all(dq == 0) and np.allclose(dk, 0, atol=1e-15)
+    np.testing.assert_allclose(dv[:, :, 0], do.sum(axis=2), rtol=1e-14)
+
+
+def test_bwd_identical_keys_give_zero_dq():
+    """With every key equal, scores are constant along each row and the softmax does not depend
+    on q: dq = 0 (the rows of dS sum to zero)."""
+    rng = np.random.default_rng(4)
+    q, do = rng.standard_normal((1, 2, 6, 8)), rng.standard_normal((1, 2, 6, 8))
+    k = np.repeat(rng.standard_normal((1, 2, 1, 8)), 5, axis=2)
+    v = rng.standard_normal((1, 2, 5, 8))
+    dq, _, _ = oracle.attention_bwd(q, k, v, do, False, 0.9)
+    np.testing.assert_allclose(dq, 0, atol=1e-13)
+
+
+def test_bwd_row_subsets_and_empty_rows():
+    """Subsets of rows give the same values as the full run; a causal row with no allowed key
+    (Nq > Nk) has dq = 0 and changes no dk / dv."""
+    rng = np.random.default_rng(5)
+    q, k, v, do = (rng.standard_normal(s) for s in [(1, 2, 9, 8), (1, 2, 6, 8), (1, 2, 6, 8), (1, 2, 9, 8)])
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, True, 0.5)
+    qr, kr = np.array([8, 0, 4]), np.array([5, 1])
+    sq, sk, sv = oracle.attention_bwd(q, k, v, do, True, 0.5, q_rows=qr, k_rows=kr)
+    np.testing.assert_array_equal(sq, dq[:, :, qr])
+    np.testing.assert_array_equal(sk, dk[:, :, kr])
+    np.testing.assert_array_equal(sv, dv[:, :, kr])
+    assert np.all(dq[:, :, :3] == 0)  # rows 0..2 see keys <= i - 3 < 0
+    do2 = do.copy()
+    do2[:, :, :3] = rng.standard_normal((1, 2, 3, 8))
+    _, dk2, dv2 = oracle.attention_bwd(q, k, v, do2, True, 0.5)
+    np.testing.assert_array_equal(dk2, dk)
+    np.testing.assert_array_equal(dv2, dv)
