@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     FP8_TILE,
     AttnError,
     abi_version,
+    attn_bwd,
     attn_fwd,
     attn_fwd_f32,
     attn_fwd_fp8,
@@ -20,6 +21,7 @@ from ._lib import (  # noqa: F401
     attn_fwd_kvblock,
     attn_fwd_ring,
     attn_merge,
+    bwd_work_floats,
     lib,
     ring_work_floats,
     status_str,

@@ -52,6 +52,10 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd_kvblock.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i64, i64, f, vp]
     L.attn_merge.restype = i
     L.attn_merge.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
+    L.attn_bwd_work_floats.restype = ctypes.c_size_t
+    L.attn_bwd_work_floats.argtypes = [i, i, i]
+    L.attn_bwd.restype = i
+    L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
     L.attn_ring_work_floats.restype = ctypes.c_size_t
     L.attn_ring_work_floats.argtypes = [i, i, i, i]
     L.attn_fwd_ring.restype = i
@@ -159,6 +163,27 @@ def attn_merge(o_acc, m_acc, l_acc, o_part, m_part, l_part, o_final=None, lse_fi
     _check(lib().attn_merge(_ptr(o_acc), _ptr(m_acc), _ptr(l_acc), _ptr(o_part), _ptr(m_part),
                             _ptr(l_part), _ptr(o_final), _ptr(lse_final), B, H, Nq, d,
                             _stream(stream)), "attn_merge")
+
+
+def bwd_work_floats(B: int, H: int, Nq: int) -> int:
+    """Size (fp32 elements) of the workspace attn_bwd needs."""
+    return int(lib().attn_bwd_work_floats(B, H, Nq))
+
+
+def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, work, causal: bool, scale: float, stream=None):
+    """Gradients of sum(dout * O): q/o/dout/dq bf16 [B,H,Nq,d], k/v/dk/dv bf16 [B,H,Nk,d],
+    lse fp32 [B,H,Nq] from attn_fwd, work fp32 of bwd_work_floats(B,H,Nq)."""
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    for t, n in ((q, "q"), (o, "o"), (dout, "dout"), (dq, "dq")):
+        _want(t, torch.bfloat16, (B, H, Nq, d), n)
+    for t, n in ((k, "k"), (v, "v"), (dk, "dk"), (dv, "dv")):
+        _want(t, torch.bfloat16, (B, H, Nk, d), n)
+    _want(lse, torch.float32, (B, H, Nq), "lse")
+    _want(work, torch.float32, (bwd_work_floats(B, H, Nq),), "work")
+    _check(lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                          _ptr(dv), _ptr(work), B, H, Nq, Nk, d, int(bool(causal)), float(scale),
+                          _stream(stream)), "attn_bwd")
 
 
 def ring_work_floats(B: int, H: int, Nq: int, d: int) -> int:

@@ -253,6 +253,38 @@ attn_status attn_fwd_ring(const void* q, const void* const* k_blks, const void* 
   return ATTN_OK;
 }
 
+size_t attn_bwd_work_floats(int B, int H, int Nq) {
+  if (B <= 0 || H <= 0 || Nq <= 0) return 0;
+  return size_t(B) * size_t(H) * size_t(Nq);
+}
+
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv, float* work, int B, int H, int Nq, int Nk,
+                     int d, int causal, float scale, void* stream) {
+  if (attn_status s = check_shape(B, H, Nq, Nk, d)) return s;
+  if (attn_status s = check_ptrs16({q, k, v, o, dout, dq, dk, dv})) return s;
+  if (attn_status s = check_ptrs4({lse, work}, false)) return s;
+  if (!std::isfinite(scale)) return ATTN_ERR_INVALID;
+  eta::BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.delta = work;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.BH = B * H;
+  p.diag = Nk - Nq;
+  p.scale = scale;
+  p.c = float(double(scale) * 1.4426950408889634074);  // log2(e)
+  return from_hip(eta::launch_bwd(p, d, causal != 0, (hipStream_t)stream));
+}
+
 static attn_status fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
                            const float* k_scale, const float* v_scale, float* o, float* lse, int B, int H,
                            int Nq, int Nk, int d, int causal, float scale, void* stream, bool qk16) {

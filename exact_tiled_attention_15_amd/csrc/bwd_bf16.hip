@@ -1,0 +1,411 @@
+// bf16 attention backward for gfx950: dQ, dK, dV of L = sum(dO * O) from the
+// saved log-sum-exp, with P recomputed tile by tile (never stored).  The pages
+// report training throughput for FlashAttention-2 ("FlashAttention-2",
+// Systems analysis wiki, "Performance and efficiency") and a training backward
+// for FlashAttention-4 ("Hardware-Aware FP4 FlashAttention-4"), which
+// presuppose this pass; they give no formula, so it is the chain rule applied
+// to the forward's definition:
+//   P_ij = exp(scale q_i.k_j - LSE_i)      dV_j = sum_i P_ij dO_i
+//   dP_ij = dO_i . v_j    D_i = dO_i . O_i = sum_j P_ij dP_ij
+//   dS_ij = P_ij (dP_ij - D_i)   dQ_i = scale sum_j dS_ij k_j
+//   dK_j = scale sum_i dS_ij q_i
+//
+// Three kernels:
+//   bwd_delta_kernel  D_i = dO_i . O_i (fp32), one pass over dO and O.
+//   bwd_dq_kernel     query rows stationary (8 wavefronts x 32 rows); K, K^T
+//                     and V stream through LDS in 64-key tiles.  S^T = K Q^T
+//                     and dP^T = V dO^T put one query per lane, so LSE_i and
+//                     D_i are per-lane scalars; dQ^T += K^T dS^T takes dS^T
+//                     straight from the accumulators as the B operand, with
+//                     K^T stored transposed and key-permuted in LDS exactly as
+//                     the forward stores V^T (common.h).
+//   bwd_dkdv_kernel   key rows stationary (4 wavefronts x 32 keys, one per
+//                     SIMD, so the two fp32 accumulators fit); Q, Q^T, dO,
+//                     dO^T, LSE and D stream through LDS in 64-query tiles.
+//                     S = Q K^T and dP = dO V^T put one key per lane;
+//                     dV^T += dO^T P and dK^T += Q^T dS take P and dS from the
+//                     accumulators, with dO^T and Q^T stored transposed and
+//                     query-permuted.
+// Probabilities and dS are rounded to bf16 for the products, accumulations are
+// fp32.  Masked (query, key) pairs get p = 0 by selection, so any finite
+// scale works.  Keys and queries beyond the tensor ends are zero-filled.
+#include "common.h"
+
+namespace eta {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634074f;
+
+__device__ inline bf16x8 pack8(const float* x) {
+  typedef float f32x8 __attribute__((ext_vector_type(8)));
+  f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+  return __builtin_convertvector(v, bf16x8);
+}
+
+// Row-major tile store: rows r0 .. r0+3 (4 x 16 bytes of w) at column chunk dc.
+__device__ inline void store_rows(char* tile, int pitch, int r0, int dc, const u32x4 (&w)[4]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) *(u32x4*)(tile + (r0 + r) * pitch + dc * 16) = w[r];
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ delta
+// 16 threads per row for d = 128 (8 for d = 64), 8 bf16 each, xor-shuffle sum.
+template <int D>
+__global__ void __launch_bounds__(256) bwd_delta_kernel(BwdParams p, int64_t rows) {
+  constexpr int TPR = D / 8;
+  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / TPR;
+  const int c = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 a = *(const u32x4*)((const uint16_t*)p.dout + row * D + c * 8);
+    const u32x4 b = *(const u32x4*)((const uint16_t*)p.o + row * D + c * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc += __uint_as_float(a[e] << 16) * __uint_as_float(b[e] << 16);
+      acc += __uint_as_float(a[e] & 0xffff0000u) * __uint_as_float(b[e] & 0xffff0000u);
+    }
+  }
+#pragma unroll
+  for (int m = TPR / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, TPR);
+  if (row < rows && c == 0) p.delta[row] = acc;
+}
+
+// --------------------------------------------------------------------- dQ
+template <int D>
+struct DqGeo {
+  static constexpr int W = 8, THREADS = 64 * W, BM = 32 * W, BN = 64, KB = BN / 32;
+  static constexpr int KS = D * 2 + 16;                 // K / V row pitch
+  static constexpr int VTP = vt_pitch(BN);              // K^T row pitch
+  static constexpr int K_BYTES = BN * KS, KT_BYTES = D * VTP, V_BYTES = BN * KS;
+  static constexpr int STAGE = K_BYTES + KT_BYTES + V_BYTES;
+  static constexpr int LDS = 2 * STAGE;
+  static constexpr int KG = BN / 4;                     // 4-key groups per tile
+  static constexpr int STAGERS = KG * (D / 8);          // per tensor (K or V)
+  static_assert(2 * STAGERS <= THREADS, "one K and one V stager per thread at most");
+};
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(512, 1) bwd_dq_kernel(BwdParams p, int nqb) {
+  using G = DqGeo<D>;
+  __shared__ __attribute__((aligned(16))) char smem[G::LDS];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r32 = lane & 31, g = lane >> 5;
+  int qb, bh;
+  map_block(blockIdx.x, nqb, p.BH, CAUSAL, qb, bh);
+  const int Nq = p.Nq, Nk = p.Nk;
+  const int q0 = qb * G::BM, qw0 = q0 + wave * 32, my_q = qw0 + r32;
+  const uint16_t* __restrict__ qg = (const uint16_t*)p.q + (int64_t)bh * Nq * D;
+  const uint16_t* __restrict__ dog = (const uint16_t*)p.dout + (int64_t)bh * Nq * D;
+  const uint16_t* __restrict__ kg = (const uint16_t*)p.k + (int64_t)bh * Nk * D;
+  const uint16_t* __restrict__ vg = (const uint16_t*)p.v + (int64_t)bh * Nk * D;
+
+  int kend = Nk;
+  if (CAUSAL) kend = min(Nk, min(q0 + G::BM, Nq) - 1 + p.diag + 1);
+  const int ntiles = kend > 0 ? (kend + G::BN - 1) / G::BN : 0;
+
+  // Stationary: Q and dO of this lane's query row (B operands), LSE and D.
+  bf16x8 qf[D / 16], dof[D / 16];
+  const bool row_ok = my_q < Nq;
+  {
+    const int64_t rq = (int64_t)(row_ok ? my_q : 0) * D + g * 8;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      qf[kk] = __builtin_bit_cast(bf16x8, row_ok ? *(const u32x4*)(qg + rq + kk * 16) : z);
+      dof[kk] = __builtin_bit_cast(bf16x8, row_ok ? *(const u32x4*)(dog + rq + kk * 16) : z);
+    }
+  }
+  const int64_t grow = (int64_t)bh * Nq + my_q;
+  const float lse_raw = row_ok ? p.lse[grow] : -INFINITY;
+  const bool has_keys = lse_raw != -INFINITY;
+  const float lse2 = has_keys ? lse_raw * kLog2e : 0.f;
+  const float dlt = row_ok ? p.delta[grow] : 0.f;
+  const float c = p.c;
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc[db] = (f32x16){};
+
+  // Staging: thread (tensor, dc, kgrp) holds keys 4*kgrp .. +3, columns 8*dc .. +7.
+  const int st = tid / G::STAGERS;  // 0: K, 1: V, 2+: idle
+  const int su = tid - st * G::STAGERS, s_kg = su % G::KG, s_dc = su / G::KG;
+  u32x4 sreg[4];
+  auto stage_base = [&](int t) { return smem + (t & 1) * G::STAGE; };
+  auto gload = [&](int t) {
+    if (st > 1) return;
+    const uint16_t* src = st == 0 ? kg : vg;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = t * G::BN + 4 * s_kg + r;
+      sreg[r] = key < Nk ? *(const u32x4*)(src + (int64_t)key * D + s_dc * 8) : (u32x4){0u, 0u, 0u, 0u};
+    }
+  };
+  auto lstore = [&](int t) {
+    char* b = stage_base(t);
+    if (st == 0) {
+      store_rows(b, G::KS, 4 * s_kg, s_dc, sreg);
+      store_vt(b + G::K_BYTES, G::VTP, 8 * s_dc, s_kg, sreg);
+    } else if (st == 1) {
+      store_rows(b + G::K_BYTES + G::KT_BYTES, G::KS, 4 * s_kg, s_dc, sreg);
+    }
+  };
+
+  const int r_off = r32 * G::KS + g * 16;    // row r32 of a 32-row block, 16-byte slice g
+  const int t_off = r32 * G::VTP + g * 16;   // transposed tile: row r32 of a 32-row block, slot 8g
+
+  if (ntiles > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const bool more = t + 1 < ntiles;
+    if (more) gload(t + 1);
+    const char* kb = stage_base(t);
+    const char* ktb = kb + G::K_BYTES;
+    const char* vb = ktb + G::KT_BYTES;
+#pragma unroll
+    for (int h = 0; h < G::KB; ++h) {
+      f32x16 s = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const bf16x8 a = *(const bf16x8*)(kb + h * 32 * G::KS + r_off + kk * 32);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s, 0, 0, 0);
+        const bf16x8 b = *(const bf16x8*)(vb + h * 32 * G::KS + r_off + kk * 32);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, dof[kk], dp, 0, 0, 0);
+      }
+      float ds[16];
+      const int kbase = t * G::BN + 32 * h + 4 * g;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kbase + 8 * (i >> 2) + (i & 3);
+        const bool ok = has_keys && key < Nk && (!CAUSAL || key <= my_q + p.diag);
+        const float pr = ok ? fast_exp2(fmaf(s[i], c, -lse2)) : 0.f;
+        ds[i] = pr * (dp[i] - dlt);
+      }
+      const bf16x8 pd[2] = {pack8(ds), pack8(ds + 8)};
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const bf16x8 a = *(const bf16x8*)(ktb + db * 32 * G::VTP + t_off + (32 * h + 16 * half) * 2);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pd[half], acc[db], 0, 0, 0);
+        }
+    }
+    if (more) lstore(t + 1);
+    __syncthreads();
+  }
+
+  if (!row_ok) return;
+  uint16_t* out = (uint16_t*)p.dq + grow * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      f32x4 v = {acc[db][4 * r] * p.scale, acc[db][4 * r + 1] * p.scale, acc[db][4 * r + 2] * p.scale,
+                 acc[db][4 * r + 3] * p.scale};
+      *(bf16x4*)(out + 32 * db + 8 * r + 4 * g) = __builtin_convertvector(v, bf16x4);
+    }
+}
+
+// ----------------------------------------------------------------- dK, dV
+template <int D>
+struct DkvGeo {
+  static constexpr int W = 4, THREADS = 64 * W, BK = 32 * W, BM = 64, QB = BM / 32;
+  static constexpr int KS = D * 2 + 16;                 // Q / dO row pitch
+  static constexpr int VTP = vt_pitch(BM);              // Q^T / dO^T row pitch
+  static constexpr int R_BYTES = BM * KS, T_BYTES = D * VTP;
+  static constexpr int STAGE = 2 * R_BYTES + 2 * T_BYTES + 2 * BM * 4;  // Q, dO, Q^T, dO^T, LSE2, D
+  static constexpr int LDS = 2 * STAGE;
+  static constexpr int QG = BM / 4;                     // 4-query groups per tile
+  static constexpr int STAGERS = QG * (D / 8);          // per tensor
+  static_assert(STAGERS <= THREADS, "one Q and one dO block per thread at most");
+  static_assert(2 * BM <= THREADS, "LSE and D loaded by one thread each");
+};
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) {
+  using G = DkvGeo<D>;
+  __shared__ __attribute__((aligned(16))) char smem[G::LDS];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r32 = lane & 31, g = lane >> 5;
+  int kb_idx, bh;
+  // key blocks in ascending order come first: under a causal mask the first
+  // keys are seen by the most queries
+  map_block(blockIdx.x, nkb, p.BH, false, kb_idx, bh);
+  const int Nq = p.Nq, Nk = p.Nk;
+  const int k0 = kb_idx * G::BK, kw0 = k0 + wave * 32, my_k = kw0 + r32;
+  const uint16_t* __restrict__ qg = (const uint16_t*)p.q + (int64_t)bh * Nq * D;
+  const uint16_t* __restrict__ dog = (const uint16_t*)p.dout + (int64_t)bh * Nq * D;
+  const uint16_t* __restrict__ kg = (const uint16_t*)p.k + (int64_t)bh * Nk * D;
+  const uint16_t* __restrict__ vg = (const uint16_t*)p.v + (int64_t)bh * Nk * D;
+  const float* __restrict__ lseg = p.lse + (int64_t)bh * Nq;
+  const float* __restrict__ dltg = p.delta + (int64_t)bh * Nq;
+
+  // Queries that see some key of this block: i >= k0 - diag under the mask.
+  const int q_first = CAUSAL ? max(0, k0 - p.diag) : 0;
+  const int t0 = q_first / G::BM;
+  const int ntiles = q_first < Nq ? (Nq + G::BM - 1) / G::BM : 0;
+
+  // Stationary: K and V of this lane's key (B operands).
+  bf16x8 kf[D / 16], vf[D / 16];
+  const bool key_ok = my_k < Nk;
+  {
+    const int64_t rk = (int64_t)(key_ok ? my_k : 0) * D + g * 8;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      kf[kk] = __builtin_bit_cast(bf16x8, key_ok ? *(const u32x4*)(kg + rk + kk * 16) : z);
+      vf[kk] = __builtin_bit_cast(bf16x8, key_ok ? *(const u32x4*)(vg + rk + kk * 16) : z);
+    }
+  }
+  const float c = p.c;
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dk[db] = dv[db] = (f32x16){};
+
+  // Staging: thread (dc, qgrp) holds queries 4*qgrp .. +3, columns 8*dc .. +7
+  // of Q and of dO; threads 0 .. BM-1 also fetch LSE2, BM .. 2BM-1 fetch D.
+  const bool stager = tid < G::STAGERS;
+  const int s_qg = tid % G::QG, s_dc = tid / G::QG;
+  u32x4 qreg[4], dreg[4];
+  float sval = 0.f;
+  auto stage_base = [&](int t) { return smem + (t & 1) * G::STAGE; };
+  auto gload = [&](int t) {
+    if (stager) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int q = t * G::BM + 4 * s_qg + r;
+        const bool ok = q < Nq;
+        const int64_t off = (int64_t)(ok ? q : 0) * D + s_dc * 8;
+        qreg[r] = ok ? *(const u32x4*)(qg + off) : (u32x4){0u, 0u, 0u, 0u};
+        dreg[r] = ok ? *(const u32x4*)(dog + off) : (u32x4){0u, 0u, 0u, 0u};
+      }
+    }
+    if (tid < 2 * G::BM) {
+      const int q = t * G::BM + (tid % G::BM);
+      if (tid < G::BM) {
+        const float l = q < Nq ? lseg[q] : -INFINITY;
+        sval = l == -INFINITY ? 0.f : l * kLog2e;  // rows without keys are masked anyway
+      } else {
+        sval = q < Nq ? dltg[q] : 0.f;
+      }
+    }
+  };
+  auto lstore = [&](int t) {
+    char* b = stage_base(t);
+    if (stager) {
+      store_rows(b, G::KS, 4 * s_qg, s_dc, qreg);
+      store_rows(b + G::R_BYTES, G::KS, 4 * s_qg, s_dc, dreg);
+      store_vt(b + 2 * G::R_BYTES, G::VTP, 8 * s_dc, s_qg, qreg);
+      store_vt(b + 2 * G::R_BYTES + G::T_BYTES, G::VTP, 8 * s_dc, s_qg, dreg);
+    }
+    if (tid < 2 * G::BM) ((float*)(b + 2 * G::R_BYTES + 2 * G::T_BYTES))[tid] = sval;
+  };
+
+  const int r_off = r32 * G::KS + g * 16;
+  const int t_off = r32 * G::VTP + g * 16;
+
+  if (ntiles > t0) {
+    gload(t0);
+    lstore(t0);
+  }
+  __syncthreads();
+  for (int t = t0; t < ntiles; ++t) {
+    const bool more = t + 1 < ntiles;
+    if (more) gload(t + 1);
+    const char* qb = stage_base(t);
+    const char* dob = qb + G::R_BYTES;
+    const char* qtb = qb + 2 * G::R_BYTES;
+    const char* dotb = qtb + G::T_BYTES;
+    const float* l2 = (const float*)(dotb + G::T_BYTES);
+    const float* dl = l2 + G::BM;
+#pragma unroll
+    for (int h = 0; h < G::QB; ++h) {
+      f32x16 s = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const bf16x8 a = *(const bf16x8*)(qb + h * 32 * G::KS + r_off + kk * 32);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[kk], s, 0, 0, 0);
+        const bf16x8 b = *(const bf16x8*)(dob + h * 32 * G::KS + r_off + kk * 32);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, vf[kk], dp, 0, 0, 0);
+      }
+      // element i: query 32h + 8(i/4) + 4g + i%4 of the tile, key my_k
+      float pr[16], ds[16];
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const int ql = 32 * h + 8 * blk + 4 * g;
+        const f32x4 lv = *(const f32x4*)(l2 + ql);
+        const f32x4 dv4 = *(const f32x4*)(dl + ql);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * blk + e;
+          const int q = t * G::BM + ql + e;
+          const bool ok = key_ok && q < Nq && (!CAUSAL || my_k <= q + p.diag);
+          pr[i] = ok ? fast_exp2(fmaf(s[i], c, -lv[e])) : 0.f;
+          ds[i] = pr[i] * (dp[i] - dv4[e]);
+        }
+      }
+      const bf16x8 pp[2] = {pack8(pr), pack8(pr + 8)};
+      const bf16x8 pd[2] = {pack8(ds), pack8(ds + 8)};
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int off = db * 32 * G::VTP + t_off + (32 * h + 16 * half) * 2;
+          const bf16x8 a = *(const bf16x8*)(dotb + off);
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pp[half], dv[db], 0, 0, 0);
+          const bf16x8 b = *(const bf16x8*)(qtb + off);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, pd[half], dk[db], 0, 0, 0);
+        }
+    }
+    if (more) lstore(t + 1);
+    __syncthreads();
+  }
+
+  if (!key_ok) return;
+  const int64_t grow = (int64_t)bh * Nk + my_k;
+  uint16_t* outk = (uint16_t*)p.dk + grow * D;
+  uint16_t* outv = (uint16_t*)p.dv + grow * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      f32x4 a = {dk[db][4 * r] * p.scale, dk[db][4 * r + 1] * p.scale, dk[db][4 * r + 2] * p.scale,
+                 dk[db][4 * r + 3] * p.scale};
+      f32x4 b = {dv[db][4 * r], dv[db][4 * r + 1], dv[db][4 * r + 2], dv[db][4 * r + 3]};
+      *(bf16x4*)(outk + 32 * db + 8 * r + 4 * g) = __builtin_convertvector(a, bf16x4);
+      *(bf16x4*)(outv + 32 * db + 8 * r + 4 * g) = __builtin_convertvector(b, bf16x4);
+    }
+}
+
+// --------------------------------------------------------------- launcher
+template <int D>
+static hipError_t launch_bwd_d(const BwdParams& p, bool causal, hipStream_t s) {
+  const int64_t rows = (int64_t)p.BH * p.Nq;
+  const int64_t dblocks = (rows * (D / 8) + 255) / 256;
+  hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)dblocks), dim3(256), 0, s, p, rows);
+  if (hipError_t e = hipGetLastError()) return e;
+  const int nkb = (p.Nk + DkvGeo<D>::BK - 1) / DkvGeo<D>::BK;
+  const int nqb = (p.Nq + DqGeo<D>::BM - 1) / DqGeo<D>::BM;
+  const dim3 gkv((unsigned)(nkb * p.BH)), gq((unsigned)(nqb * p.BH));
+  if (causal) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), gkv, dim3(DkvGeo<D>::THREADS), 0, s, p, nkb);
+    if (hipError_t e = hipGetLastError()) return e;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), gq, dim3(DqGeo<D>::THREADS), 0, s, p, nqb);
+  } else {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), gkv, dim3(DkvGeo<D>::THREADS), 0, s, p, nkb);
+    if (hipError_t e = hipGetLastError()) return e;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), gq, dim3(DqGeo<D>::THREADS), 0, s, p, nqb);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t s) {
+  if (d == 128) return launch_bwd_d<128>(p, causal, s);
+  if (d == 64) return launch_bwd_d<64>(p, causal, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace eta

@@ -85,6 +85,28 @@ struct MergeParams {
 };
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);
 
+// Backward pass (gradients of sum(dO * O)).  All tensors [B,H,N,d] bf16 except
+// lse (fp32 [B,H,Nq], natural log, as the forward writes it) and delta (fp32
+// [B,H,Nq] workspace: D_i = dO_i . O_i).
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* delta;
+  void* dq;
+  void* dk;
+  void* dv;
+  int Nq, Nk;
+  int BH;
+  int diag;      // causal: key j allowed for row i iff j <= i + diag
+  float scale;   // any finite value
+  float c;       // scale * log2(e)
+};
+hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t s);
+
 // ------------------------------------------------------------ device helpers
 // Workgroup -> (query block, b*h slice).  Workgroups are dealt to the 8 XCDs
 // round-robin (XCD = blockIdx % 8); when the slices divide evenly, each XCD is

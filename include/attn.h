@@ -134,6 +134,31 @@ attn_status attn_merge(float* o_acc, float* m_acc, float* l_acc,
                        int B, int H, int Nq, int d, void* stream);
 
 /*
+ * attn_bwd - gradients of L = sum(dO * O) with respect to q, k and v for the
+ * attention that attn_fwd computes, from its output and log-sum-exp; the
+ * probabilities are recomputed tile by tile and never stored.  The pages give
+ * training results that presuppose this pass ("FlashAttention-2",
+ * "Performance and efficiency"; the FlashAttention-4 summary's training
+ * backward) but no formula: it is the chain rule applied to the forward,
+ *   P = exp(scale q.k - LSE),  dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),
+ *   dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+ *   q, o, dout      bf16 [B,H,Nq,d]     k, v  bf16 [B,H,Nk,d]
+ *   lse             fp32 [B,H,Nq]  as attn_fwd writes it (natural log,
+ *                   including scale; -inf for rows without keys)
+ *   dq              bf16 [B,H,Nq,d]     dk, dv  bf16 [B,H,Nk,d]  (outputs)
+ *   work            device fp32 workspace of attn_bwd_work_floats(B,H,Nq)
+ *                   floats (receives D), owned by the caller
+ * causal and scale as in attn_fwd (any finite scale).  Products run on bf16
+ * matrix cores with fp32 accumulation; P and dS are rounded to bf16 for them.
+ * Errors: as attn_fwd, plus ATTN_ERR_INVALID for a NULL lse or work.
+ */
+size_t attn_bwd_work_floats(int B, int H, int Nq);
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                     float* work, int B, int H, int Nq, int Nk, int d, int causal,
+                     float scale, void* stream);
+
+/*
  * attn_fwd_ring - one GPU's whole share of ring attention ("Sequence
  * parallelism and ring attention", "Deep dive" and "Technical insight"):
  * the local query shard against the K/V blocks that the ring's hops deliver,

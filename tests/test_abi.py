@@ -121,3 +121,18 @@ def test_ring_validation():
     assert ring(w=MIS) == eta.ATTN_ERR_INVALID             # misaligned workspace
     assert ring(d=96) == eta.ATTN_ERR_UNSUPPORTED
     assert ring(scale=float("nan")) == eta.ATTN_ERR_INVALID
+
+
+def test_bwd_validation():
+    """attn_bwd rejects bad arguments before any launch."""
+    L = eta.lib()
+    assert L.attn_bwd_work_floats(2, 3, 5) == 30
+    assert L.attn_bwd_work_floats(2, 0, 5) == 0
+    P = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(8)]
+    bwd = lambda lse=P4, work=ctypes.c_void_p(0x900004), d=64, scale=0.1, dq=P[5]: L.attn_bwd(
+        P[0], P[1], P[2], P[3], P[4], lse, dq, P[6], P[7], work, 1, 2, 8, 8, d, 1, scale, None)
+    assert bwd(lse=NUL) == eta.ATTN_ERR_INVALID
+    assert bwd(work=NUL) == eta.ATTN_ERR_INVALID
+    assert bwd(dq=MIS) == eta.ATTN_ERR_INVALID
+    assert bwd(d=96) == eta.ATTN_ERR_UNSUPPORTED
+    assert bwd(scale=float("inf")) == eta.ATTN_ERR_INVALID

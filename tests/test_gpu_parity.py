@@ -336,6 +336,91 @@ def test_workload_kv_blocks():
     compare_o(o_1[:, :, rows], ro, BF16_BAR, "one-pass vs oracle")
 
 
+# ------------------------------------------------------------- backward
+def compare_grad(got, ref, what, rel_bar=1e-2, abs_frac=2e-2):
+    """Gradients: relative Frobenius error <= 1e-2 and max-abs error <= 2 % of the largest
+    reference magnitude.  The kernels round P and dS to bf16 (2^-9 relative) inside fp32
+    sums and round the outputs to bf16 (2^-9): about 0.2-0.4 % is expected."""
+    err = np.abs(got - ref)
+    big = float(np.abs(ref).max()) if ref.size else 0.0
+    nref = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(got - ref) / nref) if nref > 0 else float(np.linalg.norm(got))
+    m = float(err.max()) if err.size else 0.0
+    say(f"  {what}: max_abs={m:.3e} (max|ref|={big:.3f}) rel_frob={rel:.3e}")
+    assert np.all(np.isfinite(got)), f"{what}: non-finite"
+    assert rel <= rel_bar, f"{what}: rel_frob {rel:.3e} > {rel_bar}"
+    assert m <= abs_frac * max(big, 1e-6), f"{what}: max_abs {m:.3e} > {abs_frac} * {big:.3e}"
+
+
+def _run_bwd(qb, kb, vb, ob, dob, lse, causal, scale):
+    q, k, v, o, do = (dev_bf16(x) for x in (qb, kb, vb, ob, dob))
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    dq = torch.full((B, H, Nq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dk = torch.full((B, H, Nk, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dv = torch.full((B, H, Nk, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    work = torch.full((eta.bwd_work_floats(B, H, Nq),), float("nan"), device="cuda")
+    eta.attn_bwd(q, k, v, o, do, lse if torch.is_tensor(lse) else dev(lse), dq, dk, dv, work, causal, scale)
+    torch.cuda.synchronize()
+    return host(dq), host(dk), host(dv)
+
+
+BWD_SHAPES = [
+    (1, 2, 128, 128, 128, False, 0.0884),
+    (1, 2, 200, 333, 128, True, 0.0884),
+    (2, 1, 300, 300, 64, True, 0.125),
+    (1, 2, 65, 31, 64, True, 0.125),      # Nq > Nk: rows without keys
+    (1, 2, 257, 513, 128, False, 0.0884),  # ragged tiles on both sides
+    (1, 1, 1, 1, 128, False, 0.0884),
+    (1, 2, 96, 160, 128, True, -0.2),
+    (1, 2, 96, 160, 64, False, 0.0),
+]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d,causal,scale", BWD_SHAPES)
+def test_bwd_small_shapes(B, H, Nq, Nk, d, causal, scale):
+    """attn_bwd against the fp64 gradient; O and LSE are the oracle's (O rounded to bf16), so
+    only the backward kernels are under test."""
+    say(f"bwd B={B} H={H} Nq={Nq} Nk={Nk} d={d} causal={causal} scale={scale}")
+    seed = 7 * Nq + Nk + d
+    qb, kb, vb = _bf16_problem(B, H, Nq, Nk, d, seed)
+    dob = inputs.bf16_bits(inputs.normal_f32((B, H, Nq, d), seed, 6))
+    qd, kd, vd, dod = (oracle.decode_bf16(x) for x in (qb, kb, vb, dob))
+    ro, rl = oracle.attention(qd, kd, vd, causal, scale)
+    ob = inputs.bf16_bits(ro.astype(np.float32))
+    dq, dk, dv = _run_bwd(qb, kb, vb, ob, dob, rl.astype(np.float32), causal, scale)
+    rdq, rdk, rdv = oracle.attention_bwd(qd, kd, vd, dod, causal, scale)
+    compare_grad(dq, rdq, "dQ")
+    compare_grad(dk, rdk, "dK")
+    compare_grad(dv, rdv, "dV")
+
+
+def test_bwd_headline_shape_end_to_end():
+    """Training step of the headline shape: attn_fwd's O and LSE feed attn_bwd; sampled dQ rows
+    and dK/dV rows against the fp64 gradient."""
+    name = "bf16_causal_B8_H16_N2048_d128"
+    say(f"bwd {name}")
+    cfg, seed = configs.WORKLOADS[name], configs.seed_of(name)
+    scale = configs.scale_of(name)
+    x = inputs.make_inputs(cfg, seed)
+    B, H, N, d = cfg["B"], cfg["H"], cfg["Nq"], cfg["d"]
+    dob = inputs.bf16_bits(inputs.normal_f32((B, H, N, d), seed, 6))
+    q, k, v = dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"])
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), device="cuda")
+    eta.attn_fwd(q, k, v, o, lse, True, scale)
+    torch.cuda.synchronize()
+    ob = o.view(torch.int16).cpu().numpy().view(np.uint16)
+    dq, dk, dv = _run_bwd(x["q"], x["k"], x["v"], ob, dob, lse, True, scale)
+    qr = _sample_rows(N, 64, seed)
+    kr = _sample_rows(N, 64, seed + 1)
+    qd, kd, vd, dod = (oracle.decode_bf16(a) for a in (x["q"], x["k"], x["v"], dob))
+    rdq, rdk, rdv = oracle.attention_bwd(qd, kd, vd, dod, True, scale, q_rows=qr, k_rows=kr)
+    compare_grad(dq[:, :, qr], rdq, f"dQ ({len(qr)} rows/head)")
+    compare_grad(dk[:, :, kr], rdk, f"dK ({len(kr)} rows/head)")
+    compare_grad(dv[:, :, kr], rdv, f"dV ({len(kr)} rows/head)")
+
+
 # ------------------------------------------------------- ring-attention share
 def _ring_run(q, k_full, v_full, blk, order, causal, q_pos0, scale):
     """attn_fwd_ring over the blocks of k_full / v_full (blk keys each) in the given hop order."""
