@@ -111,7 +111,18 @@ def main():
     bf = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
     dv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
-    if dtype == "bf16" and "n_blocks" not in cfg:
+    if dtype == "bf16" and cfg.get("backward"):
+        q, k, v = bf(x["q"]), bf(x["k"]), bf(x["v"])
+        do = bf(inputs.bf16_bits(inputs.normal_f32((B, H, Nq, d), seed, 6)))
+        o = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((B, H, Nq), device="cuda")
+        eta.attn_fwd(q, k, v, o, lse, causal, scale, stream)  # the forward the gradients belong to
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        work = torch.empty((eta.bwd_work_floats(B, H, Nq),), device="cuda")
+        step = lambda: eta.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, work, causal, scale, stream)
+        kernel = "bwd_delta_kernel + bwd_dkdv_kernel + bwd_dq_kernel"
+        launches = 3
+    elif dtype == "bf16" and "n_blocks" not in cfg:
         q, k, v = bf(x["q"]), bf(x["k"]), bf(x["v"])
         o = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device="cuda")
         lse = torch.empty((B, H, Nq), device="cuda")
@@ -210,7 +221,9 @@ def main():
         cpu = cpu_baseline(name, cfg, seed, x, args.cpu_seconds)
 
     out = {
-        "metric": "attention fwd TFLOP/s (bf16 d=128, causal) and % of MI355X dense MFMA peak",
+        "metric": ("attention bwd TFLOP/s (bf16 d=128, causal; FLOPs = 2.5x the forward's) and % of MI355X "
+                   "dense MFMA peak" if cfg.get("backward") else
+                   "attention fwd TFLOP/s (bf16 d=128, causal) and % of MI355X dense MFMA peak"),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -259,12 +272,24 @@ def cpu_baseline(name, cfg, seed, x, target_s):
     keys_probe = float(sum((i + Nk - Nq + 1) if causal else Nk for i in probe_rows))
     keys_head = float(sum((i + Nk - Nq + 1) if causal else Nk for i in range(Nq)))
     t_head = max(t_probe * keys_head / keys_probe, 1e-6)
+    backward = bool(cfg.get("backward"))
+    if backward:  # the gradient costs about four forward passes in the oracle
+        t_head *= 4.0
+        from exact_tiled_attention_15_amd import inputs
+        dob = inputs.bf16_bits(inputs.normal_f32((B, H, Nq, d), seed, 6))
     n_heads = int(max(1, min(B * H, target_s / t_head)))
     flop = 0.0
     elapsed = 0.0  # oracle time only; decoding the slice's inputs is not counted
     for u in range(n_heads):
         b, h = divmod(u, H)
         q, k, v = head(b, h)
+        if backward:
+            do = oracle.decode_bf16(dob[b:b + 1, h:h + 1])
+            tt = time.perf_counter()
+            oracle.attention_bwd(q, k, v, do, causal, scale)
+            elapsed += time.perf_counter() - tt
+            flop += 2.5 * 4.0 * d * keys_head
+            continue
         tt = time.perf_counter()
         oracle.attention(q, k, v, causal, scale)
         elapsed += time.perf_counter() - tt
@@ -274,7 +299,8 @@ def cpu_baseline(name, cfg, seed, x, target_s):
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": f"{n_heads} of {B * H} (b,h) slices, all {Nq} rows x {'causal' if causal else 'all'} keys, "
+        "sample": f"{n_heads} of {B * H} (b,h) slices, all {Nq} rows x {'causal' if causal else 'all'} keys"
+                  f"{', gradients dq/dk/dv' if backward else ''}, "
                   f"fp64, {elapsed:.1f} s on {cpu_model()}",
         "flop": flop,
         "seconds": round(elapsed, 3),

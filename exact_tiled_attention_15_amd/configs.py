@@ -28,6 +28,10 @@ WORKLOADS = {
     "bf16_causal_ring_B1_H16_N65536_R8_d128": dict(index=5, B=1, H=16, Nq=8192, Nk=65536, d=128,
                                                    dtype="bf16", causal=True, n_blocks=8,
                                                    q_pos0=57344, ring=True, oracle_rows=256),
+    # The backward pass (dQ, dK, dV from the saved LSE) of the GPT-style causal shape; dO
+    # is a seeded N(0,1) draw (sub-stream 6).
+    "bwd_bf16_causal_B8_H16_N2048_d128": dict(index=6, B=8, H=16, Nq=2048, Nk=2048, d=128,
+                                              dtype="bf16", causal=True, backward=True),
     # Block-quantized e4m3 with 1% outlier channels (x20), optional Hadamard rotation.
     "fp8_B4_H16_N4096_d128": dict(index=4, B=4, H=16, Nq=4096, Nk=4096, d=128, dtype="fp8",
                                   causal=False, outlier_frac=0.01, outlier_mult=20.0,
@@ -62,9 +66,13 @@ def ring_hops(name: str):
 
 def workload_flops(name: str) -> float:
     """FLOPs credited to one pass of a workload: the metric convention, except that a
-    causal ring share counts its allowed (query, key) pairs exactly."""
+    causal ring share counts its allowed (query, key) pairs exactly and a backward pass
+    counts 2.5 times its forward (the usual convention for attention training)."""
     cfg = WORKLOADS[name]
     B, H, Nq, Nk, d = cfg["B"], cfg["H"], cfg["Nq"], cfg["Nk"], cfg["d"]
+    if cfg.get("backward"):
+        # five matrix products of 2 Nq Nk d each against the forward's two
+        return 2.5 * flops(B, H, Nq, Nk, d, cfg["causal"])
     if cfg.get("ring") and cfg["causal"]:
         q0 = cfg["q_pos0"]
         pairs = Nq * q0 + Nq * (Nq + 1) // 2  # row q0 + i sees keys 0 .. q0 + i

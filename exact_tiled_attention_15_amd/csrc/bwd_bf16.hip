@@ -321,16 +321,32 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) 
     const char* dotb = qtb + G::T_BYTES;
     const float* l2 = (const float*)(dotb + G::T_BYTES);
     const float* dl = l2 + G::BM;
+    // S and dP of both 32-query blocks: 4 (D/16) MFMA chains, LDS reads run
+    // four fragments ahead.
+    f32x16 s[G::QB], dp[G::QB];
+#pragma unroll
+    for (int h = 0; h < G::QB; ++h) s[h] = dp[h] = (f32x16){};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int h = 0; h < G::QB; ++h) {
+        const bf16x8 a = *(const bf16x8*)(qb + h * 32 * G::KS + r_off + kk * 32);
+        s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[kk], s[h], 0, 0, 0);
+        const bf16x8 b = *(const bf16x8*)(dob + h * 32 * G::KS + r_off + kk * 32);
+        dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, vf[kk], dp[h], 0, 0, 0);
+      }
+    {
+      constexpr int NM = 2 * G::QB * (D / 16);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < NM - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
 #pragma unroll
     for (int h = 0; h < G::QB; ++h) {
-      f32x16 s = (f32x16){}, dp = (f32x16){};
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 a = *(const bf16x8*)(qb + h * 32 * G::KS + r_off + kk * 32);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[kk], s, 0, 0, 0);
-        const bf16x8 b = *(const bf16x8*)(dob + h * 32 * G::KS + r_off + kk * 32);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, vf[kk], dp, 0, 0, 0);
-      }
       // element i: query 32h + 8(i/4) + 4g + i%4 of the tile, key my_k
       float pr[16], ds[16];
 #pragma unroll
@@ -343,8 +359,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) 
           const int i = 4 * blk + e;
           const int q = t * G::BM + ql + e;
           const bool ok = key_ok && q < Nq && (!CAUSAL || my_k <= q + p.diag);
-          pr[i] = ok ? fast_exp2(fmaf(s[i], c, -lv[e])) : 0.f;
-          ds[i] = pr[i] * (dp[i] - dv4[e]);
+          pr[i] = ok ? fast_exp2(fmaf(s[h][i], c, -lv[e])) : 0.f;
+          ds[i] = pr[i] * (dp[h][i] - dv4[e]);
         }
       }
       const bf16x8 pp[2] = {pack8(pr), pack8(pr + 8)};
@@ -359,6 +375,16 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) 
           const bf16x8 b = *(const bf16x8*)(qtb + off);
           dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, pd[half], dk[db], 0, 0, 0);
         }
+      {
+        constexpr int NM = 2 * 2 * (D / 32);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < NM - 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      }
     }
     if (more) lstore(t + 1);
     __syncthreads();
