@@ -107,7 +107,7 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
 
-    x = inputs.make_inputs(cfg, seed)
+    x = inputs.make_inputs(cfg, seed, rotate=cfg.get("rotate", False))
     bf = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
     dv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
@@ -176,8 +176,9 @@ def main():
         t = {n: dv(x[n]) for n in ("q8", "k8", "v8", "q_scale", "k_scale", "v_scale")}
         o = torch.empty((B, H, Nq, d), device="cuda")
         lse = torch.empty((B, H, Nq), device="cuda")
-        step = lambda: eta.attn_fwd_fp8(t["q8"], t["k8"], t["v8"], t["q_scale"], t["k_scale"], t["v_scale"],
-                                        o, lse, causal, scale, stream)
+        fp8_fn = eta.attn_fwd_fp8_pv8 if cfg.get("pv8") else eta.attn_fwd_fp8
+        step = lambda: fp8_fn(t["q8"], t["k8"], t["v8"], t["q_scale"], t["k_scale"], t["v_scale"],
+                              o, lse, causal, scale, stream)
         kernel = "fwd_fp8_kernel"
         launches = 1
 

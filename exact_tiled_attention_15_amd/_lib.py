@@ -60,7 +60,7 @@ def lib() -> ctypes.CDLL:
     L.attn_ring_work_floats.argtypes = [i, i, i, i]
     L.attn_fwd_ring.restype = i
     L.attn_fwd_ring.argtypes = [vp, vp, vp, vp, i, vp, vp, vp, i, i, i, i, i, i, i64, f, vp]
-    for name in ("attn_fwd_fp8", "attn_fwd_fp8_qk16"):
+    for name in ("attn_fwd_fp8", "attn_fwd_fp8_qk16", "attn_fwd_fp8_pv8"):
         fn = getattr(L, name)
         fn.restype = i
         fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
@@ -245,3 +245,9 @@ def attn_fwd_fp8_qk16(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, causal: boo
                       stream=None):
     """As attn_fwd_fp8 with QK^T on fp16 matrix cores over exactly widened codes."""
     _fwd_fp8("attn_fwd_fp8_qk16", q8, k8, v8, q_scale, k_scale, v_scale, o, lse, causal, scale, stream)
+
+
+def attn_fwd_fp8_pv8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, causal: bool, scale: float,
+                     stream=None):
+    """As attn_fwd_fp8 with P in e4m3 and P.V on fp8 matrix cores (faster, drifts by P's rounding)."""
+    _fwd_fp8("attn_fwd_fp8_pv8", q8, k8, v8, q_scale, k_scale, v_scale, o, lse, causal, scale, stream)

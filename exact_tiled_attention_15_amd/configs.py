@@ -33,9 +33,14 @@ WORKLOADS = {
     "bwd_bf16_causal_B8_H16_N2048_d128": dict(index=6, B=8, H=16, Nq=2048, Nk=2048, d=128,
                                               dtype="bf16", causal=True, backward=True),
     # Block-quantized e4m3 with 1% outlier channels (x20), optional Hadamard rotation.
+    # Timed with the rotation applied (the fp8 matrix cores need it on outlier channels).
     "fp8_B4_H16_N4096_d128": dict(index=4, B=4, H=16, Nq=4096, Nk=4096, d=128, dtype="fp8",
                                   causal=False, outlier_frac=0.01, outlier_mult=20.0,
-                                  oracle_rows=512),
+                                  oracle_rows=512, rotate=True),
+    # The same recipe with the probabilities in e4m3 too (both products on fp8 matrix cores).
+    "fp8_pv8_B4_H16_N4096_d128": dict(index=7, B=4, H=16, Nq=4096, Nk=4096, d=128, dtype="fp8",
+                                      causal=False, outlier_frac=0.01, outlier_mult=20.0,
+                                      oracle_rows=512, rotate=True, pv8=True),
 }
 
 HEADLINE = "bf16_causal_B8_H16_N2048_d128"

@@ -287,7 +287,7 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
 
 static attn_status fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
                            const float* k_scale, const float* v_scale, float* o, float* lse, int B, int H,
-                           int Nq, int Nk, int d, int causal, float scale, void* stream, bool qk16) {
+                           int Nq, int Nk, int d, int causal, float scale, void* stream, int mode) {
   if (attn_status s = check_shape(B, H, Nq, Nk, d)) return s;
   if (attn_status s = check_ptrs16({q8, k8, v8, o})) return s;
   if (attn_status s = check_ptrs4({q_scale, k_scale, v_scale}, false)) return s;
@@ -302,19 +302,28 @@ static attn_status fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* 
   p.v_scale = v_scale;
   p.o = o;
   p.lse = lse;
-  return from_hip(eta::launch_fwd_fp8(p, d, causal != 0, qk16, (hipStream_t)stream));
+  return from_hip(eta::launch_fwd_fp8(p, d, causal != 0, mode, (hipStream_t)stream));
 }
 
 attn_status attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
                          const float* k_scale, const float* v_scale, float* o, float* lse, int B, int H,
                          int Nq, int Nk, int d, int causal, float scale, void* stream) {
-  return fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, Nq, Nk, d, causal, scale, stream, false);
+  return fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, Nq, Nk, d, causal, scale, stream,
+                 eta::kFp8QkFp8);
 }
 
 attn_status attn_fwd_fp8_qk16(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
                               const float* k_scale, const float* v_scale, float* o, float* lse, int B, int H,
                               int Nq, int Nk, int d, int causal, float scale, void* stream) {
-  return fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, Nq, Nk, d, causal, scale, stream, true);
+  return fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, Nq, Nk, d, causal, scale, stream,
+                 eta::kFp8QkFp16);
+}
+
+attn_status attn_fwd_fp8_pv8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
+                             const float* k_scale, const float* v_scale, float* o, float* lse, int B, int H,
+                             int Nq, int Nk, int d, int causal, float scale, void* stream) {
+  return fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, Nq, Nk, d, causal, scale, stream,
+                 eta::kFp8AllFp8);
 }
 
 }  // extern "C"

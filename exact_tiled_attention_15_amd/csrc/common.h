@@ -69,7 +69,10 @@ struct FwdParams {
 // Launchers (host side). Each returns hipGetLastError() after the launch.
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, int epi, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t s);
-hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, bool qk16, hipStream_t s);
+// fp8 forward modes: QK^T on fp8 or fp16 matrix cores (P.V on fp16), or both
+// products on fp8 matrix cores.
+enum Fp8Mode : int { kFp8QkFp8 = 0, kFp8QkFp16 = 1, kFp8AllFp8 = 2 };
+hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, int mode, hipStream_t s);
 
 struct MergeParams {
   float* o_acc;

@@ -22,6 +22,19 @@
 //     p * s_v(t) / max_t s_v (the ratio folded into the exponent bias, so the
 //     value is <= 1 for any scales), and the normaliser is summed from the
 //     unrounded fp32 values with the ratio divided out once per tile.
+//   * PV8 instantiation (the FlashAttention-3 FP8 form of the same passage,
+//     probabilities in fp8 too): P V on the 32x32x64 f8f6f4 MFMA with V's
+//     codes used as they are.  A lane's 32 scores of a 64-key group are
+//     exactly the 32 bytes its B operand needs, so P goes from the
+//     accumulators into e4m3 bytes with no data movement; V^T is stored in
+//     LDS as codes, keys permuted so that the A operand's k order matches
+//     (common slot formula in vt8_slot below).  P is quantized as
+//     p * s_v(t) / max s_v * 2^8 (<= 256 < 448, and small probabilities stay
+//     representable) and the MFMA's E8M0 block scale 2^-8 on P undoes the
+//     factor exactly; the normaliser sums the rounded values.  e4m3 keeps 3
+//     mantissa bits, so this trades accuracy for speed: the result drifts from
+//     exact attention by the rounding of P (measured, not held to the parity
+//     bar).
 //   * O accumulates and is written in fp32.
 // For the f8f6f4 MFMA the A/B k-slice of lane l is bytes (l/32)*32 .. +32.
 #include "common.h"
@@ -30,7 +43,7 @@ namespace eta {
 
 constexpr int kQuantTile = 128;  // tokens per quantization tile
 
-template <int D, bool QK16, int W, int BN>
+template <int D, bool QK16, bool PV8, int W, int BN>
 struct Geo8 {
   static constexpr int THREADS = 64 * W;
   static constexpr int BM = 32 * W;
@@ -39,7 +52,8 @@ struct Geo8 {
   static constexpr int KROW = QK16 ? 2 * D : D;   // bytes of one staged K row
   static constexpr int KS = KROW + 16;            // K tile row pitch (bytes)
   static constexpr int K_BYTES = BN * KS;
-  static constexpr int V_BYTES = D * VTP;         // fp16 V^T: one row per column d
+  static constexpr int VTP8 = BN + 16;            // fp8 V^T row pitch (bytes)
+  static constexpr int V_BYTES = PV8 ? D * VTP8 : D * VTP;  // V^T: one row per column d
   static constexpr int LDS = 2 * K_BYTES + 2 * V_BYTES;
   static constexpr int CPR = D / 16;              // 16-byte code chunks per row
   static constexpr int K_SLOTS = KS / 16;         // 16-byte LDS slots per K row (pad included)
@@ -48,6 +62,7 @@ struct Geo8 {
   static constexpr int KG = BN / 4;
   static constexpr int V_THREADS = KG * (D / 8);
   static_assert(BN <= kQuantTile && kQuantTile % BN == 0, "a tile must sit inside one scale tile");
+  static_assert(!PV8 || (BN % 64 == 0 && !QK16), "fp8 P.V works on 64-key groups, with fp8 QK^T");
   static_assert(QK16 ? (K_PER_THREAD >= 1 && K_PER_THREAD * THREADS == BN * CPR)
                      : (K_LOADS * 64 == BN * K_SLOTS), "K tile must split evenly");
   static_assert(V_THREADS <= THREADS, "V staging needs at most one thread per 4x8 block");
@@ -74,9 +89,35 @@ __device__ inline u32x4 widen_hi(const u32x4 w) {  // codes 8..15 of 16 -> fp16
   return r;
 }
 
-template <int D, bool CAUSAL, bool QK16, int W, int BN>
+// Byte slot of key k within its 64-key group in the fp8 V^T tile: the order in
+// which a lane's S^T accumulator elements of two 32-key blocks become the 32
+// bytes of the f8f6f4 B operand (block b = k / 32, element i of the block
+// with k % 32 = 8 (i / 4) + 4 g + i % 4, byte 32 g + 16 b + i).
+__host__ __device__ constexpr int vt8_slot(int k) {
+  return 64 * (k >> 6) + 32 * ((k >> 2) & 1) + 16 * ((k >> 5) & 1) + 4 * ((k >> 3) & 3) + (k & 3);
+}
+
+// Four keys x 8 codes (w[r] = codes of key 4kg + r, columns d0 .. d0+7) into
+// fp8 V^T rows d0 .. d0+7: one 4-byte word per row (bytes = keys 4kg .. +3).
+__device__ inline void store_vt8(char* vt, int pitch, int d0, int kg, const u32x2 (&w)[4]) {
+  const int col = vt8_slot(4 * kg);
+#pragma unroll
+  for (int hw = 0; hw < 2; ++hw) {  // codes 0..3 / 4..7 of each key
+    const uint32_t k0 = w[0][hw], k1 = w[1][hw], k2 = w[2][hw], k3 = w[3][hw];
+    const uint32_t t0 = __builtin_amdgcn_perm(k1, k0, 0x05010400u);  // k0.b0 k1.b0 k0.b1 k1.b1
+    const uint32_t t1 = __builtin_amdgcn_perm(k1, k0, 0x07030602u);  // k0.b2 k1.b2 k0.b3 k1.b3
+    const uint32_t t2 = __builtin_amdgcn_perm(k3, k2, 0x05010400u);
+    const uint32_t t3 = __builtin_amdgcn_perm(k3, k2, 0x07030602u);
+    const uint32_t r[4] = {__builtin_amdgcn_perm(t2, t0, 0x05040100u), __builtin_amdgcn_perm(t2, t0, 0x07060302u),
+                           __builtin_amdgcn_perm(t3, t1, 0x05040100u), __builtin_amdgcn_perm(t3, t1, 0x07060302u)};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) *(uint32_t*)(vt + (d0 + 4 * hw + e) * pitch + col) = r[e];
+  }
+}
+
+template <int D, bool CAUSAL, bool QK16, bool PV8, int W, int BN>
 __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
-  using G = Geo8<D, QK16, W, BN>;
+  using G = Geo8<D, QK16, PV8, W, BN>;
   constexpr int QT = kQuantTile;
   __shared__ __attribute__((aligned(16))) char smem[G::LDS];
 
@@ -202,6 +243,10 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
   };
   auto lstore_v = [&](int t) {
     if (!v_stager) return;
+    if constexpr (PV8) {
+      store_vt8(vstage(t), G::VTP8, 8 * v_dc, v_kg, vreg);
+      return;
+    }
     u32x4 w[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) w[r] = widen_lo((u32x4){vreg[r][0], vreg[r][1], 0u, 0u});
@@ -301,47 +346,86 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
       // P' = p * s_v(t) / s_v_max: the tile's V scale rides in the exponent
       // bias; the normaliser gets p back through one multiply per tile.
       const float bias_v = ((m2 == -INFINITY) ? 0.f : -m2) + vfold;
-      // P' = exp2(...) in fp16 and O^T += V^T P'^T, one 32-key block h at a
-      // time: block h's MFMAs need only block h's probabilities, so the
-      // exponentials of block h+1 issue between them.  Four partial sums.
-      float rs[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (PV8) {
+        // P' * 2^8 in e4m3 and O^T += V^T P'^T on the f8f6f4 MFMA, one 64-key
+        // group at a time (4 MFMAs per group at d = 128).  The normaliser
+        // sums the rounded values (2^-8 applied once per tile).
+        float rs[4] = {0.f, 0.f, 0.f, 0.f};
+        const float bias8 = bias_v + 8.f;  // * 2^8
 #pragma unroll
-      for (int h = 0; h < G::KB; ++h) {
-        f16x8 pb[2];
+        for (int grp = 0; grp < G::KB / 2; ++grp) {
+          i32x8 pb8;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          f32x8 pv;
+          for (int b = 0; b < 2; ++b)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float e = fast_exp2(fmaf(s[h][half * 8 + j], c, bias_v));  // masked: exp2(-inf) = 0
-            pv[j] = e;
-            rs[j & 3] += e;
+            for (int j = 0; j < 4; ++j) {  // dword 4b + j = elements 4j .. 4j+3 of block 2 grp + b
+              const f32x16& sv = s[2 * grp + b];
+              const float e0 = fast_exp2(fmaf(sv[4 * j], c, bias8)), e1 = fast_exp2(fmaf(sv[4 * j + 1], c, bias8));
+              const float e2 = fast_exp2(fmaf(sv[4 * j + 2], c, bias8)), e3 = fast_exp2(fmaf(sv[4 * j + 3], c, bias8));
+              int w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+              w = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
+              pb8[4 * b + j] = w;
+              const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+              const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+              rs[0] += lo[0];
+              rs[1] += lo[1];
+              rs[2] += hi[0];
+              rs[3] += hi[1];
+            }
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const char* ap = vstage(t) + (32 * db + r32) * G::VTP8 + 64 * grp + 32 * g;
+            const u32x4 a0 = *(const u32x4*)ap;
+            const u32x4 a1 = *(const u32x4*)(ap + 16);
+            const i32x8 av = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                              (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+            oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb8, oacc[db], 0, 0, 0, 127, 0, 119);
           }
-          pb[half] = __builtin_convertvector(pv, f16x8);
         }
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
+        l_lane += ((rs[0] + rs[1]) + (rs[2] + rs[3])) * (vunfold * 0.00390625f);
+      } else {
+        // P' = exp2(...) in fp16 and O^T += V^T P'^T, one 32-key block h at a
+        // time: block h's MFMAs need only block h's probabilities, so the
+        // exponentials of block h+1 issue between them.  Four partial sums.
+        float rs[4] = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+        for (int h = 0; h < G::KB; ++h) {
+          f16x8 pb[2];
+  #pragma unroll
           for (int half = 0; half < 2; ++half) {
-            const f16x8 a = *(const f16x8*)(vstage(t) + v_off + db * 32 * G::VTP + (32 * h + 16 * half) * 2);
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[half], oacc[db], 0, 0, 0);
+            f32x8 pv;
+  #pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float e = fast_exp2(fmaf(s[h][half * 8 + j], c, bias_v));  // masked: exp2(-inf) = 0
+              pv[j] = e;
+              rs[j & 3] += e;
+            }
+            pb[half] = __builtin_convertvector(pv, f16x8);
           }
-      }
-      l_lane += ((rs[0] + rs[1]) + (rs[2] + rs[3])) * vunfold;
-      {
-        constexpr int NM = (D / 32) * G::KB * 2;
-        constexpr int VPB = 56;  // vector instructions of one block's probabilities
-        constexpr int VPM = (VPB + 2 * (D / 32) - 1) / (2 * (D / 32));
-        __builtin_amdgcn_sched_group_barrier(0x002, VPB, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-        for (int i = 0; i < NM; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (i + 4 < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+  #pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+  #pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              const f16x8 a = *(const f16x8*)(vstage(t) + v_off + db * 32 * G::VTP + (32 * h + 16 * half) * 2);
+              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[half], oacc[db], 0, 0, 0);
+            }
+        }
+        l_lane += ((rs[0] + rs[1]) + (rs[2] + rs[3])) * vunfold;
+        {
+          constexpr int NM = (D / 32) * G::KB * 2;
+          constexpr int VPB = 56;  // vector instructions of one block's probabilities
+          constexpr int VPM = (VPB + 2 * (D / 32) - 1) / (2 * (D / 32));
+          __builtin_amdgcn_sched_group_barrier(0x002, VPB, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+  #pragma unroll
+          for (int i = 0; i < NM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (i + 4 < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+          }
         }
       }
-    }
+      }
     if (more) {
       store_k(t + 1);
       lstore_v(t + 1);
@@ -367,21 +451,31 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
   }
 }
 
-template <int D, bool QK16>
+template <int D, bool QK16, bool PV8>
 static hipError_t launch_fp8_d(FwdParams p, bool causal, hipStream_t s) {
   constexpr int W = kWavesBf16, BN = kTileBf16;
   p.nqb = (p.Nq + 32 * W - 1) / (32 * W);
   const dim3 grid((unsigned)(p.nqb * p.BH));
   if (causal)
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, true, QK16, W, BN>), grid, dim3(64 * W), 0, s, p);
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, true, QK16, PV8, W, BN>), grid, dim3(64 * W), 0, s, p);
   else
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, false, QK16, W, BN>), grid, dim3(64 * W), 0, s, p);
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, false, QK16, PV8, W, BN>), grid, dim3(64 * W), 0, s, p);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, bool qk16, hipStream_t s) {
-  if (d == 128) return qk16 ? launch_fp8_d<128, true>(p, causal, s) : launch_fp8_d<128, false>(p, causal, s);
-  if (d == 64) return qk16 ? launch_fp8_d<64, true>(p, causal, s) : launch_fp8_d<64, false>(p, causal, s);
+template <int D>
+static hipError_t launch_fp8_mode(const FwdParams& p, bool causal, int mode, hipStream_t s) {
+  switch (mode) {
+    case kFp8QkFp8: return launch_fp8_d<D, false, false>(p, causal, s);
+    case kFp8QkFp16: return launch_fp8_d<D, true, false>(p, causal, s);
+    case kFp8AllFp8: return launch_fp8_d<D, false, true>(p, causal, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, int mode, hipStream_t s) {
+  if (d == 128) return launch_fp8_mode<128>(p, causal, mode, s);
+  if (d == 64) return launch_fp8_mode<64>(p, causal, mode, s);
   return hipErrorInvalidValue;
 }
 

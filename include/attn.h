@@ -222,6 +222,23 @@ attn_status attn_fwd_fp8_qk16(const uint8_t* q8, const uint8_t* k8, const uint8_
                               float* o, float* lse, int B, int H, int Nq, int Nk, int d,
                               int causal, float scale, void* stream);
 
+/*
+ * attn_fwd_fp8_pv8 - as attn_fwd_fp8 with the probabilities in e4m3 too:
+ * both products on the fp8 matrix cores (the FlashAttention-3 FP8 form,
+ * "Scaling FlashAttention, multi-GPU training and weight quantization" §1),
+ * V's codes used as they are.  P is quantized as p * s_v / max s_v * 2^8 and
+ * the matrix core's block scale 2^-8 undoes the factor exactly; the
+ * normaliser sums the rounded values.  e4m3 keeps 3 mantissa bits, so the
+ * result drifts from exact attention by the rounding of P: a speed-for-
+ * accuracy mode (the drift is measured and reported, not held to the fp8
+ * parity bar).  Same arguments and errors as attn_fwd_fp8; for inputs with
+ * outlier channels apply the rotation, as for attn_fwd_fp8.
+ */
+attn_status attn_fwd_fp8_pv8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                             const float* q_scale, const float* k_scale, const float* v_scale,
+                             float* o, float* lse, int B, int H, int Nq, int Nk, int d,
+                             int causal, float scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
