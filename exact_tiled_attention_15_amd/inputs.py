@@ -1,6 +1,6 @@
 """Seeded synthetic inputs, shared by the GPU path's tests/benchmark and the
 CPU oracle's.  This module draws and encodes numbers only; it holds none of
-the attention arithmetic.
+the arithmetic of attention or of the W4A16 layer.
 
 * Normal draws: numpy PCG64 ``default_rng([seed, stream])``.
 * bfloat16: round-to-nearest-even of the float32 draw (bit patterns, uint16).
@@ -11,6 +11,12 @@ the attention arithmetic.
   same random orthogonal matrix M = H_d diag(sigma) / sqrt(d) (Sylvester
   Hadamard, seeded signs) multiplies Q and K on the right, so Q K^T is
   unchanged in exact arithmetic.
+* W4A16 layer inputs (same page, section 3): every 32-bit word is a valid
+  packing of eight 4-bit codes, so packed weights are uniform random words;
+  zero points are uniform in 0..15, scales uniform in [2e-3, 6e-3] rounded to
+  float16, activations N(0, 1) rounded to float16.  The "exact" variant draws
+  integer activations in -4..4 and power-of-two scales 2^-7..2^-3, so every
+  product and partial sum is exact in float32.
 * Block quantization (same passage: a separate scale per small tile): per
   (b, h, 128-token tile) scale s = float32(amax / 448) (1 when amax = 0), code
   = OCP e4m3 round-to-nearest-even of float32(x / s) clipped to +-448.
@@ -109,3 +115,26 @@ def make_inputs(cfg: dict, seed: int, rotate: bool = False) -> dict:
         return dict(q8=q8, k8=k8, v8=v8, q_scale=qs, k_scale=ks, v_scale=vs, channels=ch,
                     q_unquantized=q, k_unquantized=k, v_unquantized=v)
     raise ValueError(cfg["dtype"])
+
+
+def fp16_bits(x: np.ndarray) -> np.ndarray:
+    """float -> IEEE binary16 bit patterns, round to nearest even."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def make_w4a16_inputs(M: int, N: int, K: int, group: int, seed: int, exact: bool = False) -> dict:
+    """Host inputs of one W4A16 layer call: x fp16 bits [M, K], packed uint32
+    [N, K/8], zeros uint8 [N, K/group], scales fp16 bits [N, K/group]."""
+    if K % 8 or K % group:
+        raise ValueError("K must be a multiple of 8 and of the group size")
+    ng = K // group
+    g = rng(seed, 10)
+    packed = g.integers(0, 2**32, size=(N, K // 8), dtype=np.uint64).astype(np.uint32)
+    zeros = g.integers(0, 16, size=(N, ng), dtype=np.uint8)
+    if exact:
+        scales = np.exp2(g.integers(-7, -2, size=(N, ng))).astype(np.float32)
+        x = rng(seed, 11).integers(-4, 5, size=(M, K)).astype(np.float32)
+    else:
+        scales = g.uniform(2e-3, 6e-3, size=(N, ng)).astype(np.float32)
+        x = normal_f32((M, K), seed, 11)
+    return dict(x=fp16_bits(x), packed=packed, zeros=zeros, scales=fp16_bits(scales))

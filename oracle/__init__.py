@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for exact softmax attention (ctypes over attn_oracle.c).
+"""fp64 CPU oracle for exact softmax attention and the W4A16 layer (ctypes over attn_oracle.c).
 
 TEST INFRASTRUCTURE ONLY: tests/, the smoke check in __graft_entry__ and the
 CPU-baseline leg of bench.py may import this package; the library's compute
@@ -54,6 +54,10 @@ def _L():
         L.oracle_state_lse.argtypes = [vp, vp, i64, vp]
         L.oracle_num_threads.restype = i
         L.oracle_num_threads.argtypes = []
+        L.oracle_w4_value.restype = i
+        L.oracle_w4_value.argtypes = [vp, i64]
+        L.oracle_w4a16.restype = i
+        L.oracle_w4a16.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp]
         L.oracle_attention_bwd.restype = i
         L.oracle_attention_bwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i, d, vp, i64, vp, i64,
                                            vp, vp, vp]
@@ -178,3 +182,34 @@ def attention_bwd(q, k, v, dout, causal: bool, scale: float, q_rows=None, k_rows
     if rc != 0:
         raise RuntimeError(f"oracle_attention_bwd failed ({rc})")
     return dq, dk, dv
+
+
+def fp16_value(bits: np.ndarray) -> np.ndarray:
+    """IEEE binary16 bit patterns -> float64 (exact)."""
+    return np.ascontiguousarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def w4_value(row_words: np.ndarray, k: int) -> int:
+    """The 4-bit value of weight k from one row's packed words."""
+    w = np.ascontiguousarray(row_words, dtype=np.uint32)
+    return int(_L().oracle_w4_value(_p(w), int(k)))
+
+
+def w4a16(x_bits, packed, zeros, scale_bits, group: int):
+    """fp64 y [M, N] of the W4A16 layer: x fp16 bits [M, K], packed uint32 [N, K/8],
+    zeros uint8 [N, K/G], scale fp16 bits [N, K/G]."""
+    x = fp16_value(x_bits)
+    sc = fp16_value(scale_bits)
+    packed = np.ascontiguousarray(packed, dtype=np.uint32)
+    zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
+    M, K = x.shape
+    N = packed.shape[0]
+    group = int(group)
+    if group <= 0 or K % 8 or K % group or packed.shape != (N, K // 8) \
+            or zeros.shape != (N, K // group) or sc.shape != (N, K // group):
+        raise ValueError("oracle_w4a16: bad shape")
+    y = np.empty((M, N))
+    rc = _L().oracle_w4a16(_p(x), _p(packed), _p(zeros), _p(sc), M, N, K, group, _p(y))
+    if rc != 0:
+        raise ValueError("oracle_w4a16: bad shape")
+    return y

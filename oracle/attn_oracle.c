@@ -1,5 +1,5 @@
 /*
- * Plain fp64 CPU oracle for exact softmax attention.
+ * Plain fp64 CPU oracle for exact softmax attention and for the W4A16 layer.
  *
  * TEST INFRASTRUCTURE ONLY. Nothing in the library's compute path may include,
  * link, load or call this file; it exists so that tests, the smoke check and the
@@ -45,6 +45,16 @@
  *    loss L = sum_i dO_i . O_i:  dV_j = sum_i P_ij dO_i ;
  *    dP_ij = dO_i . v_j ;  D_i = sum_j P_ij dP_ij ;  dS_ij = P_ij (dP_ij - D_i) ;
  *    dQ_i = scale sum_j dS_ij k_j ;  dK_j = scale sum_i dS_ij q_i.
+ *
+ *  - The W4A16 linear layer of "Scaling FlashAttention, multi-GPU training and
+ *    weight quantization" (itimpress), section 3: weights stored as 4-bit
+ *    integers, eight to a 32-bit word, with a scale and a zero point per group,
+ *    turned back into 16-bit values as w = (q - z) * s and multiplied with
+ *    16-bit activations: y[m][n] = sum_k x[m][k] w[n][k].  The pages do not fix
+ *    the order of the eight values in a word; this project's reading (the
+ *    library's input format) puts weight k = 8j + e of row n in word j at bits
+ *    4 (e / 2) + 16 (e % 2) .. +3, so even e fill the low 16 bits and odd e the
+ *    high 16 bits.  Groups are G consecutive k of one row.
  *
  * Layout of every tensor: contiguous [B, H, N, d], d innermost; per-row outputs
  * [B, H, N].  A row subset is given as `rows` (n_rows query indices shared by
@@ -377,6 +387,39 @@ int oracle_attention_bwd(const double* q, const double* k, const double* v, cons
 #undef ORACLE_P
     free(lse);
     free(Dr);
+    return 0;
+}
+
+/* ------------------------------------------------------------ W4A16 layer */
+
+/* The 4-bit value of weight k of a row from its packed words (bit position
+ * 4 (e / 2) + 16 (e % 2) for e = k % 8 in word k / 8). */
+int oracle_w4_value(const uint32_t* row_words, int64_t k) {
+    const int64_t j = k / 8, e = k % 8;
+    const int shift = (int)(4 * (e / 2) + 16 * (e % 2));
+    return (int)((row_words[j] >> shift) & 0xFu);
+}
+
+/* y [M, N] = x [M, K] . W^T with W[n][k] = (q[n][k] - zero[n][k/G]) * scale[n][k/G];
+ * packed: [N, K/8] words, zero: [N, K/G], scale: [N, K/G] (already decoded to
+ * doubles).  K must be a multiple of 8 and of G. */
+int oracle_w4a16(const double* x, const uint32_t* packed, const uint8_t* zero, const double* scale,
+                 int64_t M, int64_t N, int64_t K, int64_t G, double* y) {
+    if (M < 0 || N < 0 || K <= 0 || G <= 0 || K % 8 || K % G) return -1;
+    const int64_t ng = K / G;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        const uint32_t* rw = packed + n * (K / 8);
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t g = k / G;
+                const double w = (double)(oracle_w4_value(rw, k) - (int)zero[n * ng + g]) * scale[n * ng + g];
+                acc += x[m * K + k] * w;
+            }
+            y[m * N + n] = acc;
+        }
+    }
     return 0;
 }
 

@@ -319,3 +319,114 @@ def test_bwd_row_subsets_and_empty_rows():
     _, dk2, dv2 = oracle.attention_bwd(q, k, v, do2, True, 0.5)
     np.testing.assert_array_equal(dk2, dk)
     np.testing.assert_array_equal(dv2, dv)
+
+
+# ---------------------------------------------------------------- W4A16 layer
+W4_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "w4a16_hand.json")
+
+
+def _pack_rows(codes):
+    """Dense codes [N, K] (0..15) -> words [N, K/8]: the even-indexed codes of
+    each run of eight fill the low 16 bits, four bits apiece, and the odd ones
+    the high 16 bits (the library's format)."""
+    codes = np.asarray(codes, dtype=np.uint32)
+    N, K = codes.shape
+    c = codes.reshape(N, K // 8, 8)
+    lo = c[..., 0] | (c[..., 2] << 4) | (c[..., 4] << 8) | (c[..., 6] << 12)
+    hi = c[..., 1] | (c[..., 3] << 4) | (c[..., 5] << 8) | (c[..., 7] << 12)
+    return (lo | (hi << 16)).astype(np.uint32)
+
+
+def _h(x):
+    return np.asarray(x, dtype=np.float16).view(np.uint16)
+
+
+def test_w4_word_layout_matches_hand_fixture():
+    g = json.load(open(W4_GOLDEN))
+    for case in g["words"]:
+        w = np.array([int(case["word"], 16)], dtype=np.uint32)
+        assert [oracle.w4_value(w, k) for k in range(8)] == case["codes"], case["word"]
+
+
+def test_w4a16_worked_example_from_hand_fixture():
+    ex = json.load(open(W4_GOLDEN))["worked_example"]
+    packed = np.array([[int(w, 16) for w in row] for row in ex["packed"]], dtype=np.uint32)
+    y = oracle.w4a16(_h(ex["x"]), packed, np.array(ex["zeros"], dtype=np.uint8), _h(ex["scales"]), ex["group"])
+    np.testing.assert_array_equal(y, np.array(ex["y"]))
+
+
+def test_w4a16_pack_roundtrip_matches_dense_matmul():
+    rng = np.random.default_rng(41)
+    M, N, K, G = 3, 5, 256, 64
+    codes = rng.integers(0, 16, size=(N, K))
+    zeros = rng.integers(0, 16, size=(N, K // G)).astype(np.uint8)
+    scales = rng.uniform(0.01, 0.1, size=(N, K // G)).astype(np.float16)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    w = (codes - np.repeat(zeros.astype(np.int64), G, axis=1)) * np.repeat(scales.astype(np.float64), G, axis=1)
+    ref = x.astype(np.float64) @ w.T
+    y = oracle.w4a16(x.view(np.uint16), _pack_rows(codes), zeros, scales.view(np.uint16), G)
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_w4a16_one_hot_activations_read_back_every_weight():
+    rng = np.random.default_rng(42)
+    N, K, G = 4, 256, 128
+    codes = rng.integers(0, 16, size=(N, K))
+    zeros = rng.integers(0, 16, size=(N, K // G)).astype(np.uint8)
+    scales = np.array(rng.choice([0.25, 0.5, 2.0, 0.125], size=(N, K // G)), dtype=np.float16)
+    y = oracle.w4a16(np.eye(K, dtype=np.float16).view(np.uint16), _pack_rows(codes), zeros,
+                     scales.view(np.uint16), G)
+    for n in range(N):
+        for k in range(K):
+            g = k // G
+            assert y[k, n] == (int(codes[n, k]) - int(zeros[n, g])) * float(scales[n, g]), (n, k)
+
+
+def test_w4a16_codes_equal_to_zero_point_give_zero():
+    N, K, G = 3, 384, 128
+    zeros = np.array([[0, 7, 15], [3, 3, 9], [15, 0, 1]], dtype=np.uint8)
+    codes = np.repeat(zeros.astype(np.int64), G, axis=1)
+    x = np.random.default_rng(43).standard_normal((2, K)).astype(np.float16)
+    y = oracle.w4a16(x.view(np.uint16), _pack_rows(codes), zeros, _h(np.ones((N, K // G))), G)
+    assert np.all(y == 0.0)
+
+
+def test_w4a16_quantized_layer_is_within_rounding_of_the_float_layer():
+    # Asymmetric 4-bit quantization of a float matrix per group of 128: each
+    # dequantized weight is within one scale step of the original, so the
+    # layer output is within sum_k |x_k| * scale of the unquantized product.
+    rng = np.random.default_rng(44)
+    M, N, K, G = 2, 6, 512, 128
+    w = rng.uniform(-0.05, 0.08, size=(N, K))
+    wg = w.reshape(N, K // G, G)
+    lo, hi = wg.min(axis=2), wg.max(axis=2)
+    s = np.float16((hi - lo) / 15.0 * (1 + 2.0**-9)).astype(np.float64)
+    z = np.clip(np.round(-lo / s), 0, 15)
+    q = np.clip(np.round(wg / s[..., None]) + z[..., None], 0, 15).reshape(N, K).astype(np.int64)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    y = oracle.w4a16(x.view(np.uint16), _pack_rows(q), z.astype(np.uint8), _h(s), G)
+    ref = x.astype(np.float64) @ w.T
+    bound = np.abs(x.astype(np.float64)) @ np.repeat(s, G, axis=1).T
+    assert np.all(np.abs(y - ref) <= bound)
+    assert np.abs(y - ref).max() > 0  # the quantization really did round
+
+
+def test_w4a16_is_linear_in_the_activations():
+    rng = np.random.default_rng(45)
+    N, K, G = 7, 256, 128
+    packed = rng.integers(0, 2**32, size=(N, K // 8), dtype=np.uint64).astype(np.uint32)
+    zeros = rng.integers(0, 16, size=(N, K // G)).astype(np.uint8)
+    scales = _h(rng.uniform(0.01, 0.1, size=(N, K // G)))
+    a = rng.integers(-8, 9, size=(1, K)).astype(np.float16)
+    b = rng.integers(-8, 9, size=(1, K)).astype(np.float16)
+    ya = oracle.w4a16(a.view(np.uint16), packed, zeros, scales, G)
+    yb = oracle.w4a16(b.view(np.uint16), packed, zeros, scales, G)
+    yab = oracle.w4a16((a + 2 * b).view(np.uint16), packed, zeros, scales, G)
+    np.testing.assert_allclose(yab, ya + 2 * yb, rtol=1e-12, atol=1e-12)
+
+
+def test_w4a16_rejects_bad_shapes():
+    x = np.zeros((1, 12), dtype=np.uint16)
+    with pytest.raises(ValueError):
+        oracle.w4a16(x, np.zeros((1, 1), dtype=np.uint32), np.zeros((1, 1), dtype=np.uint8),
+                     np.zeros((1, 1), dtype=np.uint16), 12)
