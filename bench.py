@@ -12,6 +12,12 @@ HBM before the timed region starts.  Prints one JSON line.
 The default workload is the causal bf16 B=8 H=16 N=2048 d=128 attention
 (TFLOP/s = 4*B*H*N^2*d/2 / time).  The CPU baseline is the fp64 oracle timed
 on a bounded sample of the same workload (whole heads, all rows).
+
+The W4A16 workloads (--workload w4a16_...) time one w4a16_gemm call per step,
+cycling through several copies of the weights so that every call reads its
+weights from HBM rather than from the last-level cache; the figure is GB/s of
+the bytes a call must move (packed weights, scales, zero points, activations
+in, outputs out) against the 8 TB/s HBM peak.
 """
 import argparse
 import json
@@ -28,6 +34,7 @@ if REPO not in sys.path:
     sys.path.insert(0, REPO)
 
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}  # dense MFMA, 256 CU x 2.4 GHz
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 
 # rocprofv3 FETCH_SIZE/WRITE_SIZE summaries (copy-calibrated) per workload; the
 # figure is reported only while the kernel sources still hash to the value the
@@ -99,6 +106,8 @@ def main():
 
     name = args.workload or configs.HEADLINE
     cfg = configs.WORKLOADS[name]
+    if cfg.get("kind") == "w4a16":
+        return bench_w4a16(args, name, cfg)
     seed = configs.seed_of(name)
     B, H, Nq, Nk, d = cfg["B"], cfg["H"], cfg["Nq"], cfg["Nk"], cfg["d"]
     causal = cfg["causal"]
@@ -304,6 +313,112 @@ def cpu_baseline(name, cfg, seed, x, target_s):
                   f"{', gradients dq/dk/dv' if backward else ''}, "
                   f"fp64, {elapsed:.1f} s on {cpu_model()}",
         "flop": flop,
+        "seconds": round(elapsed, 3),
+    }
+
+
+def bench_w4a16(args, name, cfg):
+    import torch
+
+    import exact_tiled_attention_15_amd as eta
+    from exact_tiled_attention_15_amd import configs, inputs
+
+    M, N, K, G = cfg["M"], cfg["N"], cfg["K"], cfg["group"]
+    copies = cfg["weight_copies"]
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    host = [inputs.make_w4a16_inputs(M, N, K, G, cfg["seed"] + 100 * c) for c in range(copies)]
+    x = torch.from_numpy(host[0]["x"].view(np.int16)).view(torch.float16).cuda()
+    ws = []
+    for h in host:
+        ws.append((torch.from_numpy(h["packed"].view(np.int32)).cuda(),
+                   torch.from_numpy(h["scales"].view(np.int16)).view(torch.float16).cuda(),
+                   torch.from_numpy(h["zeros"]).cuda()))
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    nw = eta.w4a16_work_floats(M, N, K)
+    work = torch.empty((nw,), device="cuda") if nw else None
+    state = {"i": 0}
+
+    def step():
+        p, sc, z = ws[state["i"] % copies]
+        state["i"] += 1
+        eta.w4a16_gemm(x, p, sc, z, y, work, G, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = configs.w4a16_bytes(name)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    roofline = {
+        "bound": "hbm",
+        "kernel": "w4a16_kernel" + (" + w4a16_reduce_kernel" if nw else ""),
+        "achieved": round(gbs, 1),
+        "peak": PEAK_HBM_GBS,
+        "unit": "GB/s",
+        "frac": round(gbs / PEAK_HBM_GBS, 4),
+        "traffic": measured_traffic(name),
+        "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+        "algorithmic_bytes": nbytes,
+        "launches_per_step": 2 if nw else 1,
+    }
+    cpu = None if args.no_cpu_baseline else cpu_baseline_w4a16(cfg, host[0], args.cpu_seconds)
+    out = {
+        "metric": "W4A16 decode linear layer GB/s (packed 4-bit weights + group scales/zero points + fp16 "
+                  "activations and outputs) and % of MI355X HBM peak",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": f"synthetic (seeded random 4-bit codes, scales and zero points; N(0,1) activations; "
+                f"{copies} weight copies in rotation)",
+        "config": {"workload": name, "M": M, "N": N, "K": K, "group": G, "seed": cfg["seed"]},
+        "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "wall_s_timed": round(t_wall, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_w4a16(cfg, h, target_s):
+    """The fp64 oracle on a subset of weight rows (all tokens, all of K), sized to ~target_s."""
+    import oracle
+    from exact_tiled_attention_15_amd import inputs
+
+    M, N, K, G = cfg["M"], cfg["N"], cfg["K"], cfg["group"]
+    probe = inputs.row_subset(N, 64, seed=12)
+    t0 = time.perf_counter()
+    oracle.w4a16(h["x"], h["packed"][probe], h["zeros"][probe], h["scales"][probe], G)
+    t_probe = max(time.perf_counter() - t0, 1e-6)
+    R = int(max(64, min(N, 64 * target_s / t_probe)))
+    rows = inputs.row_subset(N, R, seed=13)
+    p, z, sc = h["packed"][rows], h["zeros"][rows], h["scales"][rows]
+    t0 = time.perf_counter()
+    oracle.w4a16(h["x"], p, z, sc, G)
+    elapsed = time.perf_counter() - t0
+    nbytes = R * (K // 2 + (K // G) * 3) + M * K * 2 + M * R * 2
+    return {
+        "value": round(nbytes / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{R} of {N} weight rows, all {M} tokens x {K} inputs, fp64, {elapsed:.1f} s on {cpu_model()}",
+        "bytes": nbytes,
         "seconds": round(elapsed, 3),
     }
 

@@ -1,4 +1,5 @@
-"""Exact, IO-aware attention forward for AMD Instinct MI355X (gfx950).
+"""Exact, IO-aware attention forward for AMD Instinct MI355X (gfx950), and the
+W4A16 linear layer (4-bit weights widened in registers).
 
 The compute lives in libattn.so (hand-written HIP kernels behind the C ABI of
 include/attn.h); this package is its thin Python binding plus the seeded
@@ -11,6 +12,8 @@ from ._lib import (  # noqa: F401
     ATTN_ERR_UNSUPPORTED,
     ATTN_OK,
     FP8_TILE,
+    W4A16_GROUP,
+    W4A16_MAX_M,
     AttnError,
     abi_version,
     attn_bwd,
@@ -26,4 +29,6 @@ from ._lib import (  # noqa: F401
     lib,
     ring_work_floats,
     status_str,
+    w4a16_gemm,
+    w4a16_work_floats,
 )

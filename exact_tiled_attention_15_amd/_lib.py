@@ -1,4 +1,4 @@
-"""ctypes binding of libattn.so (include/attn.h).
+"""ctypes binding of libattn.so (include/attn.h, include/w4a16.h).
 
 Argument marshalling only: every function here checks that the torch tensors
 it is handed have the dtype/shape/device the C entry point documents, passes
@@ -18,6 +18,8 @@ ATTN_ERR_INVALID = 1
 ATTN_ERR_UNSUPPORTED = 2
 ATTN_ERR_HIP = 3
 FP8_TILE = 128
+W4A16_GROUP = 128
+W4A16_MAX_M = 16
 
 
 class AttnError(RuntimeError):
@@ -64,6 +66,10 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.restype = i
         fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    L.w4a16_work_floats.restype = ctypes.c_size_t
+    L.w4a16_work_floats.argtypes = [i64, i64, i64, i64]
+    L.w4a16_gemm.restype = i
+    L.w4a16_gemm.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp]
     _lib = L
     return L
 
@@ -251,3 +257,28 @@ def attn_fwd_fp8_pv8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, causal: bool
                      stream=None):
     """As attn_fwd_fp8 with P in e4m3 and P.V on fp8 matrix cores (faster, drifts by P's rounding)."""
     _fwd_fp8("attn_fwd_fp8_pv8", q8, k8, v8, q_scale, k_scale, v_scale, o, lse, causal, scale, stream)
+
+
+def w4a16_work_floats(M: int, N: int, K: int, group: int = W4A16_GROUP) -> int:
+    """Size (fp32 elements) of the workspace w4a16_gemm needs (0 for none)."""
+    return int(lib().w4a16_work_floats(M, N, K, group))
+
+
+def w4a16_gemm(x, packed, scales, zeros, y, work=None, group: int = W4A16_GROUP, stream=None):
+    """y [M,N] fp16 = x [M,K] fp16 . W^T, W given as 4-bit codes: packed int32 [N,K/8] (bits as
+    uint32), scales fp16 [N,K/group], zeros uint8 [N,K/group]; work fp32 of w4a16_work_floats
+    elements (None when that is 0)."""
+    M, K = x.shape
+    N = packed.shape[0]
+    if K % 8 or K % group:
+        raise ValueError("K must be a multiple of 8 and of the group size")
+    _want(x, torch.float16, (M, K), "x")
+    _want(packed, torch.int32, (N, K // 8), "packed")
+    _want(scales, torch.float16, (N, K // group), "scales")
+    _want(zeros, torch.uint8, (N, K // group), "zeros")
+    _want(y, torch.float16, (M, N), "y")
+    nw = w4a16_work_floats(M, N, K, group)
+    if nw:
+        _want(work, torch.float32, (nw,), "work")
+    _check(lib().w4a16_gemm(_ptr(x), _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(y),
+                            _ptr(work) if nw else None, M, N, K, group, _stream(stream)), "w4a16_gemm")

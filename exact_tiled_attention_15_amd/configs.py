@@ -1,4 +1,4 @@
-"""The five synthetic workloads: shapes, dtypes, masks and seeds.
+"""The synthetic workloads: shapes, dtypes, masks and seeds.
 
 Inputs are seeded synthetic draws with these shapes and value distributions;
 no public benchmark, evaluation suite or dataset is involved.  The seed of
@@ -41,6 +41,17 @@ WORKLOADS = {
     "fp8_pv8_B4_H16_N4096_d128": dict(index=7, B=4, H=16, Nq=4096, Nk=4096, d=128, dtype="fp8",
                                       causal=False, outlier_frac=0.01, outlier_mult=20.0,
                                       oracle_rows=512, rotate=True, pv8=True),
+    # W4A16 linear layers of token-by-token decoding ("Scaling FlashAttention, multi-GPU
+    # training and weight quantization", section 3: a 70-billion-parameter model whose
+    # weights, not its arithmetic, bound each generated token).  The two shapes of a
+    # 70B-class MLP (hidden size 8192, intermediate 28672) for a batch of 16 sequences,
+    # groups of 128.  Weights are seeded random words, scales and zero points seeded
+    # draws (inputs.make_w4a16_inputs); the benchmark rotates through enough copies of
+    # the weights that none is still in the 256 MB last-level cache when it is re-read.
+    "w4a16_decode_M16_N28672_K8192_G128": dict(index=8, kind="w4a16", M=16, N=28672, K=8192,
+                                               group=128, seed=1008, weight_copies=4),
+    "w4a16_decode_M16_N8192_K28672_G128": dict(index=9, kind="w4a16", M=16, N=8192, K=28672,
+                                               group=128, seed=1009, weight_copies=4),
 }
 
 HEADLINE = "bf16_causal_B8_H16_N2048_d128"
@@ -83,3 +94,11 @@ def workload_flops(name: str) -> float:
         pairs = Nq * q0 + Nq * (Nq + 1) // 2  # row q0 + i sees keys 0 .. q0 + i
         return 4.0 * B * H * d * pairs
     return flops(B, H, Nq, Nk, d, cfg["causal"])
+
+
+def w4a16_bytes(name: str) -> int:
+    """Bytes one W4A16 call must move at least: packed weights (K/2 per row), fp16
+    scales and byte zero points per group, fp16 activations in and fp16 outputs out."""
+    cfg = WORKLOADS[name]
+    M, N, K, G = cfg["M"], cfg["N"], cfg["K"], cfg["group"]
+    return N * K // 2 + N * (K // G) * 3 + M * K * 2 + M * N * 2

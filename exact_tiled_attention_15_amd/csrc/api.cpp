@@ -2,7 +2,9 @@
 // Nothing here allocates device memory or synchronises; every check happens
 // before the first HIP call, so a rejected call has no side effect.
 #include "attn.h"
+#include "w4a16.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -113,6 +115,31 @@ bool merge_grid_ok(int64_t rows, int d) {
   const int vpr = d / 4;
   const int rpb = vpr >= 256 ? 1 : 256 / vpr;
   return (rows + rpb - 1) / rpb <= INT32_MAX;
+}
+
+// Compute units of the current device (queried once per device; 0 if unknown).
+int device_compute_units() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cu = 0;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev].store(cu, std::memory_order_relaxed);
+  return cu;
+}
+
+attn_status check_w4a16(int64_t M, int64_t N, int64_t K, int64_t group) {
+  if (M < 1 || N < 1 || K < 1 || group < 1) return ATTN_ERR_INVALID;
+  if (group != W4A16_GROUP) return ATTN_ERR_UNSUPPORTED;
+  if (K % group) return ATTN_ERR_INVALID;
+  // Keeps every row index in int and a 16-row tile of W below 4 GiB (32-bit lane offsets).
+  if (N > (int64_t(1) << 30) || K > (int64_t(1) << 24)) return ATTN_ERR_INVALID;
+  if (M > W4A16_MAX_M) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
 }
 
 }  // namespace
@@ -324,6 +351,33 @@ attn_status attn_fwd_fp8_pv8(const uint8_t* q8, const uint8_t* k8, const uint8_t
                              int Nq, int Nk, int d, int causal, float scale, void* stream) {
   return fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, Nq, Nk, d, causal, scale, stream,
                  eta::kFp8AllFp8);
+}
+
+size_t w4a16_work_floats(int64_t M, int64_t N, int64_t K, int64_t group) {
+  if (check_w4a16(M, N, K, group) != ATTN_OK) return 0;
+  return eta::w4a16_plan(M, N, K).work_floats;
+}
+
+attn_status w4a16_gemm(const void* x, const uint32_t* packed, const void* scales, const uint8_t* zeros, void* y,
+                       float* work, int64_t M, int64_t N, int64_t K, int64_t group, void* stream) {
+  if (attn_status s = check_w4a16(M, N, K, group)) return s;
+  if (attn_status s = check_ptrs16({x, packed})) return s;
+  if (!scales || !aligned(scales, 2) || !zeros || !y || !aligned(y, 2)) return ATTN_ERR_INVALID;
+  const eta::W4Plan pl = eta::w4a16_plan(M, N, K);
+  if (pl.work_floats && (!work || !aligned(work, 4))) return ATTN_ERR_INVALID;
+  const int cu = device_compute_units();
+  eta::W4Params p{};
+  p.x = static_cast<const uint16_t*>(x);
+  p.packed = packed;
+  p.scales = static_cast<const uint16_t*>(scales);
+  p.zeros = zeros;
+  p.y = static_cast<uint16_t*>(y);
+  p.part = pl.work_floats ? work : nullptr;
+  p.M = int(M);
+  p.N = int(N);
+  p.K = int(K);
+  p.NG = int(K / group);
+  return from_hip(eta::launch_w4a16(p, pl, cu > 0 ? cu : 256, (hipStream_t)stream));
 }
 
 }  // extern "C"

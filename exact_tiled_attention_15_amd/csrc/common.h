@@ -186,4 +186,25 @@ __device__ inline void store_vt(char* vt, int pitch, int d0, int kg, const u32x4
   }
 }
 
+
+// ---------------------------------------------------------------- W4A16 layer
+struct W4Params {
+  const uint16_t* x;       // fp16 [M, K]
+  const uint32_t* packed;  // [N, K/8]
+  const uint16_t* scales;  // fp16 [N, K/128]
+  const uint8_t* zeros;    // [N, K/128]
+  uint16_t* y;             // fp16 [M, N]
+  float* part;             // fp32 [S, M, N] when S > 1, else null
+  int M, N, K, NG;         // NG = K / 128
+  int S, gps, ntiles;      // set from the plan by the launcher
+};
+// How a call is cut: S splits of K of gps groups each, gw groups per
+// wavefront, ntiles 16-row tiles; work_floats = S * M * N when S > 1.
+struct W4Plan {
+  int S, gps, gw, ntiles;
+  size_t work_floats;
+};
+W4Plan w4a16_plan(int64_t M, int64_t N, int64_t K);
+hipError_t launch_w4a16(const W4Params& p, const W4Plan& pl, int compute_units, hipStream_t s);
+
 }  // namespace eta

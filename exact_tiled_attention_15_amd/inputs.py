@@ -15,8 +15,8 @@ the arithmetic of attention or of the W4A16 layer.
   packing of eight 4-bit codes, so packed weights are uniform random words;
   zero points are uniform in 0..15, scales uniform in [2e-3, 6e-3] rounded to
   float16, activations N(0, 1) rounded to float16.  The "exact" variant draws
-  integer activations in -4..4 and power-of-two scales 2^-7..2^-3, so every
-  product and partial sum is exact in float32.
+  integer activations in -2..2 and power-of-two scales 2^-7..2^-4, so every
+  product and partial sum of a layer with K below 34952 is exact in float32.
 * Block quantization (same passage: a separate scale per small tile): per
   (b, h, 128-token tile) scale s = float32(amax / 448) (1 when amax = 0), code
   = OCP e4m3 round-to-nearest-even of float32(x / s) clipped to +-448.
@@ -132,8 +132,8 @@ def make_w4a16_inputs(M: int, N: int, K: int, group: int, seed: int, exact: bool
     packed = g.integers(0, 2**32, size=(N, K // 8), dtype=np.uint64).astype(np.uint32)
     zeros = g.integers(0, 16, size=(N, ng), dtype=np.uint8)
     if exact:
-        scales = np.exp2(g.integers(-7, -2, size=(N, ng))).astype(np.float32)
-        x = rng(seed, 11).integers(-4, 5, size=(M, K)).astype(np.float32)
+        scales = np.exp2(g.integers(-7, -3, size=(N, ng))).astype(np.float32)
+        x = rng(seed, 11).integers(-2, 3, size=(M, K)).astype(np.float32)
     else:
         scales = g.uniform(2e-3, 6e-3, size=(N, ng)).astype(np.float32)
         x = normal_f32((M, K), seed, 11)

@@ -10,7 +10,7 @@ import pytest
 import exact_tiled_attention_15_amd as eta
 
 REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(REPO, "include", "attn.h")
+HEADERS = [os.path.join(REPO, "include", h) for h in ("attn.h", "w4a16.h")]
 
 P16 = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation
 P16b = ctypes.c_void_p(0x20000)
@@ -22,15 +22,17 @@ NUL = None
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b((?:attn|w4a16)_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
     assert {"attn_fwd", "attn_fwd_f32", "attn_fwd_kvblock", "attn_merge", "attn_fwd_fp8",
-            "attn_abi_version", "attn_status_str"} <= set(names)
+            "attn_abi_version", "attn_status_str", "w4a16_gemm", "w4a16_work_floats"} <= set(names)
     L = eta.lib()
     for n in names:
         assert hasattr(L, n), f"{n} not exported by libattn.so"
@@ -136,3 +138,50 @@ def test_bwd_validation():
     assert bwd(dq=MIS) == eta.ATTN_ERR_INVALID
     assert bwd(d=96) == eta.ATTN_ERR_UNSUPPORTED
     assert bwd(scale=float("inf")) == eta.ATTN_ERR_INVALID
+
+
+# ---------------------------------------------------------------- W4A16 layer
+@pytest.mark.parametrize("M,N,K,want", [
+    (16, 28672, 8192, 0),                # 64 groups: one split, y written directly
+    (16, 8192, 28672, 4 * 16 * 8192),    # 224 groups: four splits of 56
+    (1, 16, 4096, 32 * 1 * 16),          # one tile: K cut into one split per group
+    (4, 100, 1024, 8 * 4 * 100),         # seven tiles, eight groups
+    (16, 4096, 128, 0),                  # one group
+    (0, 16, 128, 0), (17, 16, 128, 0), (1, 16, 100, 0),  # rejected sizes
+])
+def test_w4a16_work_floats(M, N, K, want):
+    assert eta.w4a16_work_floats(M, N, K) == want
+
+
+def test_w4a16_work_floats_rejects_other_group_sizes():
+    assert eta.w4a16_work_floats(1, 16, 256, 64) == 0
+
+
+def w4(*, x=P16, packed=P16b, scales=P4, zeros=P4, y=P4, work=NUL, M=4, N=32, K=256, group=128):
+    return eta.lib().w4a16_gemm(x, packed, scales, zeros, y, work, M, N, K, group, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=NUL), eta.ATTN_ERR_INVALID),
+    (dict(packed=NUL), eta.ATTN_ERR_INVALID),
+    (dict(scales=NUL), eta.ATTN_ERR_INVALID),
+    (dict(zeros=NUL), eta.ATTN_ERR_INVALID),
+    (dict(y=NUL), eta.ATTN_ERR_INVALID),
+    (dict(x=MIS), eta.ATTN_ERR_INVALID),
+    (dict(packed=P4), eta.ATTN_ERR_INVALID),
+    (dict(scales=ctypes.c_void_p(0x50001)), eta.ATTN_ERR_INVALID),
+    (dict(y=ctypes.c_void_p(0x50001)), eta.ATTN_ERR_INVALID),
+    (dict(M=0), eta.ATTN_ERR_INVALID),
+    (dict(N=0), eta.ATTN_ERR_INVALID),
+    (dict(K=0), eta.ATTN_ERR_INVALID),
+    (dict(K=200), eta.ATTN_ERR_INVALID),
+    (dict(N=2**30 + 1), eta.ATTN_ERR_INVALID),
+    (dict(K=2**24 + 128), eta.ATTN_ERR_INVALID),
+    (dict(group=64, K=256), eta.ATTN_ERR_UNSUPPORTED),
+    (dict(group=0), eta.ATTN_ERR_INVALID),
+    (dict(M=17), eta.ATTN_ERR_UNSUPPORTED),
+    (dict(work=NUL, M=1, N=16, K=4096), eta.ATTN_ERR_INVALID),          # needs a workspace
+    (dict(work=ctypes.c_void_p(0x50002), M=1, N=16, K=4096), eta.ATTN_ERR_INVALID),
+])
+def test_w4a16_rejects_bad_arguments(kw, want):
+    assert w4(**kw) == want
