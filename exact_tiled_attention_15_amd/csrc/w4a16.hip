@@ -29,6 +29,7 @@
 // the page's (q - z) * s per weight; it rounds less, since the widened weights
 // are exact in fp16.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -40,6 +41,7 @@ constexpr int kW4Threads = 64 * kW4Waves;
 constexpr int kW4Group = 128;  // k per group: 16 words per row
 constexpr int kW4Rows = 16;    // rows of W per tile (one MFMA column block)
 constexpr int64_t kW4FillTarget = 256;  // workgroups wanted in flight (MI355X compute units)
+constexpr int kW4MaxSplitGroups = 8 * kW4Waves;  // groups of one K split: 8 per wavefront
 
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 
@@ -73,107 +75,196 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 // (weights): row col of the tile, same k.  D: tokens 4 * quad + i (i < 4),
 // row col.  Within a group, chunk t of lane quad is word 4 * quad + t of the
 // row, so one 16-byte load per lane brings a lane's four words of a group.
+// Weight words in flight per wavefront: a ring of D slots of one group each
+// (16 rows x 64 B per slot).  Three or four 1 KB slots per wavefront (24-32 KB
+// per compute unit) stream this access pattern fastest on MI355X; deeper
+// queues are slower.  D divides GW, so a group keeps its slot across tiles.
+template <int GW>
+constexpr int ring_depth() { return GW == 8 ? 4 : GW == 6 ? 3 : GW; }
+
 template <int GW>
 __global__ __launch_bounds__(kW4Threads) void w4a16_kernel(W4Params p) {
+  constexpr int D = ring_depth<GW>();
+  static_assert(GW % D == 0, "ring depth must divide the slots per wavefront");
+  constexpr int kTab = kW4MaxSplitGroups + 1;  // last column: zero scale for dead slots
   __shared__ float xs[kW4Waves][GW][2][16];        // per token: X'g, Xg
   __shared__ float red[2][kW4Waves][16][kW4Rows];  // per-wave partial tiles
+  __shared__ float2 sz[2][kW4Rows][kTab];          // per tile: (scale, zero point) of each group
+  // Activation staging, one group per wavefront: 16 tokens x 16 chunks of
+  // 16 B, rows padded by one chunk so the transposed reads are conflict-free.
+  __shared__ u32x4 xst[kW4Waves][16][17];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, quad = lane >> 4;
   const int gs0 = blockIdx.y * p.gps;
   const int gs1 = min(p.NG, gs0 + p.gps);
+  const int ngs = gs1 - gs0;  // groups of this split (<= kW4MaxSplitGroups)
   const int g0 = gs0 + wave * GW;
   // Groups of this wavefront: [g0, g0 + ng).  Every wavefront runs GW slots
   // over groups gb .. gb + GW - 1 with gb = min(g0, NG - GW) >= 0 (GW <= NG),
   // so every slot reads a valid group; a slot whose group is not one of this
-  // wavefront's gets zero activations and adds exactly 0.  No branch depends
-  // on ng.
+  // wavefront's gets zero activations and a zero scale, and adds exactly 0.
   const int ng = max(0, min(GW, gs1 - g0));
   const int gb = min(g0, p.NG - GW);
   const int64_t kw = p.K >> 3;  // words per row
   const uint32_t m1024 = 0x64006400u, m64 = 0x54005400u;
+  const int tstep = gridDim.x;
+  auto grp = [&](int gi) { return gb + gi; };  // group held by slot gi
 
-  u32x4 wb[GW];
-  uint32_t sb[GW], zb[GW];
-  // Loads of one tile's slots: a uniform base per tile, one 32-bit lane
-  // offset, an immediate per slot.  Rows past N re-read row N-1 and are never
-  // stored.
-  auto issue = [&](int tile, int gi) {
-    const int64_t r0 = int64_t(tile) * kW4Rows;
-    const uint32_t rr = uint32_t(min(int64_t(col), p.N - 1 - r0));
-    const char* wbase = reinterpret_cast<const char*>(p.packed) + r0 * kw * 4 + int64_t(gb) * 64;
-    const char* sbase = reinterpret_cast<const char*>(p.scales) + (r0 * p.NG + gb) * 2;
-    const char* zbase = reinterpret_cast<const char*>(p.zeros) + r0 * p.NG + gb;
-    const uint32_t woff = rr * uint32_t(kw) * 4u + uint32_t(quad) * 16u;
-    const uint32_t soff = rr * uint32_t(p.NG);
-    wb[gi] = *reinterpret_cast<const u32x4*>(wbase + woff + gi * 64);
-    sb[gi] = *reinterpret_cast<const uint16_t*>(sbase + soff * 2u + gi * 2);
-    zb[gi] = *reinterpret_cast<const uint8_t*>(zbase + soff + gi);
+  // ---- weight ring: group gi of a tile lives in slot gi % D
+  u32x4 ring[D];
+  // Per-lane address parts are 32-bit (a 16-row tile of W is below 4 GiB);
+  // 64-bit parts are wave-uniform.
+  auto row_in_tile = [&](int tile, int r) {  // rows past N re-read row N-1, never stored
+    const int rmax = int(min(int64_t(kW4Rows - 1), p.N - 1 - int64_t(tile) * kW4Rows));
+    return uint32_t(min(r, rmax));
   };
-  const int tile0 = min(int(blockIdx.x), p.ntiles - 1);
-#pragma unroll
-  for (int gi = 0; gi < GW; ++gi) issue(tile0, gi);
+  auto issue = [&](int tile, int gi) {
+    const char* wbase = reinterpret_cast<const char*>(p.packed) + (int64_t(tile) * kW4Rows * kw + grp(gi) * 16) * 4;
+    const uint32_t woff = row_in_tile(tile, col) * uint32_t(kw * 4) + uint32_t(quad) * 16u;
+    ring[gi % D] = *reinterpret_cast<const u32x4*>(wbase + woff);
+  };
 
-  // Activations of each slot's group, in A-operand layout (zero for tokens
-  // >= M and for groups that are not this wavefront's).
-  u32x4 xa[GW][4];
-  const bool live_tok = col < p.M;
-  const uint16_t* xrow = p.x + int64_t(live_tok ? col : 0) * p.K;
+  // ---- (scale, zero point) table of a tile: loaded by the whole workgroup,
+  // two entries per thread, converted once, parked in registers until the
+  // tile before it ends, then written to LDS.
+  int e_row[2], e_col[2];
+  bool e_live[2];
 #pragma unroll
-  for (int gi = 0; gi < GW; ++gi)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      xa[gi][t] = u32x4{0u, 0u, 0u, 0u};
-      const int g = gb + gi;
-      if (g >= g0 && g < g0 + ng && live_tok)
-        xa[gi][t] = *reinterpret_cast<const u32x4*>(xrow + g * kW4Group + 8 * (4 * quad + t));
-    }
-
-  // X'g (column 0: the widening offsets) and Xg (column 1: ones) per token.
-  {
-    u32x4 bc = u32x4{0u, 0u, 0u, 0u};
-    if (col == 0) bc = u32x4{m1024, m64, m1024, m64};
-    if (col == 1) bc = u32x4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
-#pragma unroll
-    for (int gi = 0; gi < GW; ++gi) {
-      f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) d = mfma16(xa[gi][t], bc, d);
-      if (col < 2) *reinterpret_cast<f32x4*>(&xs[wave][gi][col][4 * quad]) = d;
-    }
+  for (int j = 0; j < 2; ++j) {
+    const int e = threadIdx.x + j * kW4Threads;
+    e_live[j] = e < kW4Rows * ngs;
+    e_row[j] = e_live[j] ? e / ngs : 0;
+    e_col[j] = e_live[j] ? e % ngs : 0;
   }
+  uint32_t sreg[2], zreg[2];
+  auto issue_sz = [&](int tile) {
+    const int64_t base = int64_t(tile) * kW4Rows * p.NG + gs0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {  // unconditional (dead entries read entry 0): every wait stays exact
+      const uint32_t i = row_in_tile(tile, e_row[j]) * uint32_t(p.NG) + uint32_t(e_col[j]);
+      sreg[j] = (p.scales + base)[i];
+      zreg[j] = (p.zeros + base)[i];
+    }
+  };
+  auto park_sz = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (e_live[j])
+        sz[buf][e_row[j]][e_col[j]] =
+            float2{float(__builtin_bit_cast(_Float16, uint16_t(sreg[j]))), float(zreg[j] & 0xFFu)};
+  };
+  // Table column of each slot (dead slots read the zero column).
+  int tcol[GW];
+#pragma unroll
+  for (int gi = 0; gi < GW; ++gi) {
+    const int g = grp(gi);
+    tcol[gi] = (g >= g0 && g < g0 + ng) ? g - gs0 : kTab - 1;
+  }
+
+  // Prologue: this workgroup's first (scale, zero) table, its first D weight
+  // slots, then every activation load, all without waiting.  The first tile
+  // consumes the activations group by group, so they arrive while the weight
+  // stream is already running.
+  const int tile0 = min(int(blockIdx.x), p.ntiles - 1);
+  issue_sz(tile0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int gi = 0; gi < D; ++gi) issue(tile0, gi);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Activations.  A group's 16 tokens x 256 B are loaded coalesced (load j:
+  // tokens 4j..4j+3, one 16-byte chunk per lane, 8 full cache lines) and
+  // turned into the A-operand layout through LDS by the first tile.  Loading
+  // them in that layout directly touches 32 half-used lines per load and costs
+  // three times as much address-unit time.  Loads are unconditional (tokens >=
+  // M read token 0) so that every wait names its group; they run two groups
+  // ahead of the first tile, interleaved with the weight stream.
+  constexpr int kXAhead = GW < 2 ? GW : 2;
+  u32x4 xa[GW][4];
+  auto issue_x = [&](int gi) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = 4 * j + (lane >> 4);
+      const uint16_t* src = p.x + int64_t(m < p.M ? m : 0) * p.K + grp(gi) * kW4Group + 8 * (lane & 15);
+      xa[gi][j] = *reinterpret_cast<const u32x4*>(src);
+    }
+  };
+  const bool live_tok = col < p.M;
+#pragma unroll
+  for (int gi = 0; gi < kXAhead; ++gi) issue_x(gi);
+  __builtin_amdgcn_sched_barrier(0);
+
+  if (threadIdx.x < 2 * kW4Rows) sz[threadIdx.x / kW4Rows][threadIdx.x % kW4Rows][kTab - 1] = float2{0.f, 0.f};
+  park_sz(0);
+  issue_sz(min(int(blockIdx.x) + tstep, p.ntiles - 1));
   __syncthreads();
 
-  int par = 0;
-  for (int tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x) {
-    // The last tile re-loads itself (cache hits) instead of branching.
-    const int next = (tile + int(gridDim.x) < p.ntiles) ? tile + int(gridDim.x) : tile;
+  // B operand that turns a group's activations into X'g (column 0: the
+  // widening offsets) and Xg (column 1: ones) per token.
+  u32x4 bc = u32x4{0u, 0u, 0u, 0u};
+  if (col == 0) bc = u32x4{m1024, m64, m1024, m64};
+  if (col == 1) bc = u32x4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+
+  auto tile_body = [&](int tile, int par, auto first) {
+    constexpr bool kFirst = decltype(first)::value;
+    // Prefetches past the last tile re-load this tile (cache hits, no branch).
+    const int next = (tile + tstep < p.ntiles) ? tile + tstep : tile;
+    const int next2 = (tile + 2 * tstep < p.ntiles) ? tile + 2 * tstep : next;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int gi = 0; gi < GW; ++gi) {
+      if constexpr (kFirst) {
+        // Coalesced chunks -> A-operand layout (token col, chunks 4 quad + t).
+        // One staging tile per wavefront; LDS runs a wavefront's accesses in
+        // order, so the next group's writes cannot pass these reads.
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xst[wave][4 * j + (lane >> 4)][lane & 15] = xa[gi][j];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) xa[gi][t] = xst[wave][col][4 * quad + t];
+        const bool live = (grp(gi) >= g0) && (grp(gi) < g0 + ng) && live_tok;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) xa[gi][t][c] = live ? xa[gi][t][c] : 0u;
+        // X'g and Xg of this group, on the matrix cores, into this wavefront's
+        // LDS rows (read back below by the same wavefront, in order).
+        f32x4 d0 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) d0 = mfma16(xa[gi][t], bc, d0);
+        if (col < 2) *reinterpret_cast<f32x4*>(&xs[wave][gi][col][4 * quad]) = d0;
+      }
       const f32x4 xp = *reinterpret_cast<const f32x4*>(&xs[wave][gi][0][4 * quad]);
       const f32x4 xq = *reinterpret_cast<const f32x4*>(&xs[wave][gi][1][4 * quad]);
-      const float z = float(zb[gi] & 0xFFu);
-      const float s = float(__builtin_bit_cast(_Float16, uint16_t(sb[gi])));
+      const float2 sc = sz[par][col][tcol[gi]];
       u32x4 b[4];
+      const u32x4 w = ring[gi % D];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) b[t] = widen_word(wb[gi][t], m1024, m64);
+      for (int t = 0; t < 4; ++t) b[t] = widen_word(w[t], m1024, m64);
       f32x4 d;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) d[i] = fmaf(-z, xq[i], -xp[i]);
+      for (int i = 0; i < 4; ++i) d[i] = fmaf(-sc.y, xq[i], -xp[i]);
 #pragma unroll
       for (int t = 0; t < 4; ++t) d = mfma16(xa[gi][t], b[t], d);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = fmaf(s, d[i], acc[i]);
-      // The slot's registers are free now: prefetch its group of the next tile.
-      // Loads complete in issue order; keeping each slot's prefetch inside its
+      for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc.x, d[i], acc[i]);
+      // The slot is free: refill it with the group D ahead (this tile or the
+      // next).  Loads complete in issue order; keeping each refill inside its
       // own group lets every wait name exactly the slot it needs.
-      issue(next, gi);
+      if (gi + D < GW)
+        issue(tile, gi + D);
+      else
+        issue(next, gi + D - GW);
+      if constexpr (kFirst) {
+        if (gi + kXAhead < GW) issue_x(gi + kXAhead);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[par][wave][4 * quad + i][col] = acc[i];
+    park_sz(par ^ 1);  // the table of the next tile (its loads were issued a tile ago)
+    issue_sz(next2);
     __syncthreads();
     if (threadIdx.x < 16 * kW4Rows) {
       const int m = threadIdx.x / kW4Rows, c = threadIdx.x % kW4Rows;
@@ -188,6 +279,12 @@ __global__ __launch_bounds__(kW4Threads) void w4a16_kernel(W4Params p) {
           p.y[int64_t(m) * p.N + n] = __builtin_bit_cast(uint16_t, _Float16(sum));
       }
     }
+  };
+
+  tile_body(int(blockIdx.x), 0, std::true_type{});  // the grid never exceeds the tile count
+  int par = 1;
+  for (int tile = blockIdx.x + tstep; tile < p.ntiles; tile += tstep) {
+    tile_body(tile, par, std::false_type{});
     par ^= 1;
   }
 }
@@ -224,7 +321,9 @@ W4Plan w4a16_plan(int64_t M, int64_t N, int64_t K) {
   S = (NG + gps - 1) / gps;  // drop splits left empty by the rounding
   pl.S = int(S);
   pl.gps = int(gps);
-  pl.gw = int((gps + kW4Waves - 1) / kW4Waves);
+  int gw = int((gps + kW4Waves - 1) / kW4Waves);
+  if (gw == 5 || gw == 7) ++gw;  // slot rings of 3 or 4 need GW in {1, 2, 3, 4, 6, 8}
+  pl.gw = gw;
   pl.ntiles = int(ntiles);
   pl.work_floats = S > 1 ? size_t(S) * size_t(M) * size_t(N) : 0;
   return pl;
@@ -242,9 +341,7 @@ hipError_t launch_w4a16(const W4Params& p0, const W4Plan& pl, int compute_units,
     case 2: e = launch_gw<2>(p, gx, s); break;
     case 3: e = launch_gw<3>(p, gx, s); break;
     case 4: e = launch_gw<4>(p, gx, s); break;
-    case 5: e = launch_gw<5>(p, gx, s); break;
     case 6: e = launch_gw<6>(p, gx, s); break;
-    case 7: e = launch_gw<7>(p, gx, s); break;
     case 8: e = launch_gw<8>(p, gx, s); break;
     default: return hipErrorInvalidValue;
   }
