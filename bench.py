@@ -41,6 +41,7 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 # counters were taken with.
 TRAFFIC_PROFILES = {
     "bf16_causal_B8_H16_N2048_d128": "profiles/fwd_bf16_causal_B8_H16_N2048_d128_hbm_traffic.txt",
+    "w4a16_decode_M16_N28672_K8192_G128": "profiles/w4a16_decode_M16_N28672_K8192_G128_hbm_traffic.txt",
 }
 
 
@@ -356,6 +357,12 @@ def bench_w4a16(args, name, cfg):
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms = e0.elapsed_time(e1) / args.steps
+    if args.copy_calibration:
+        # plain copy of a known size: 256 MiB read + 256 MiB written
+        src = torch.ones(64 << 20, device="cuda")
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
     nbytes = configs.w4a16_bytes(name)
     gbs = nbytes / (ms * 1e-3) / 1e9
     roofline = {

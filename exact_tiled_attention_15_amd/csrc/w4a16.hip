@@ -42,6 +42,7 @@ constexpr int kW4Group = 128;  // k per group: 16 words per row
 constexpr int kW4Rows = 16;    // rows of W per tile (one MFMA column block)
 constexpr int64_t kW4FillTarget = 256;  // workgroups wanted in flight (MI355X compute units)
 constexpr int kW4MaxSplitGroups = 8 * kW4Waves;  // groups of one K split: 8 per wavefront
+constexpr int kW4ReduceUnroll = 8;               // split partials requested together
 
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 
@@ -289,14 +290,37 @@ __global__ __launch_bounds__(kW4Threads) void w4a16_kernel(W4Params p) {
   }
 }
 
-// y = fp16(sum over splits of part), splits added in order 0..S-1.
+// y = fp16(sum over splits of part), splits added in order 0..S-1; four
+// outputs per thread, vectorised when the pointers allow it.
 __global__ __launch_bounds__(256) void w4a16_reduce_kernel(const float* __restrict__ part, uint16_t* __restrict__ y,
                                                            int S, int64_t MN) {
-  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= MN) return;
-  float sum = 0.f;
-  for (int s = 0; s < S; ++s) sum += part[int64_t(s) * MN + i];
-  y[i] = __builtin_bit_cast(uint16_t, _Float16(sum));
+  const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+  const bool vec = (MN & 3) == 0 && (reinterpret_cast<uintptr_t>(part) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(y) & 7) == 0;
+  if (vec && i + 4 <= MN) {
+    // Every partial is requested before the first is added (one memory
+    // latency, not S), then they are added in split order.
+    f32x4 v[kW4ReduceUnroll];
+    f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < S; s0 += kW4ReduceUnroll) {
+#pragma unroll
+      for (int u = 0; u < kW4ReduceUnroll; ++u)
+        if (s0 + u < S) v[u] = *reinterpret_cast<const f32x4*>(part + int64_t(s0 + u) * MN + i);
+#pragma unroll
+      for (int u = 0; u < kW4ReduceUnroll; ++u)
+        if (s0 + u < S) sum = (s0 + u == 0) ? v[u] : sum + v[u];
+    }
+    uint16_t o[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] = __builtin_bit_cast(uint16_t, _Float16(sum[c]));
+    *reinterpret_cast<uint2*>(y + i) = uint2{o[0] | (uint32_t(o[1]) << 16), o[2] | (uint32_t(o[3]) << 16)};
+    return;
+  }
+  for (int64_t j = i; j < i + 4 && j < MN; ++j) {
+    float sum = part[j];
+    for (int s = 1; s < S; ++s) sum += part[int64_t(s) * MN + j];
+    y[j] = __builtin_bit_cast(uint16_t, _Float16(sum));
+  }
 }
 
 template <int GW>
@@ -347,7 +371,7 @@ hipError_t launch_w4a16(const W4Params& p0, const W4Plan& pl, int compute_units,
   }
   if (e != hipSuccess || pl.S == 1) return e;
   const int64_t MN = int64_t(p.M) * p.N;
-  hipLaunchKernelGGL(w4a16_reduce_kernel, dim3(unsigned((MN + 255) / 256)), dim3(256), 0, s, p.part, p.y, pl.S, MN);
+  hipLaunchKernelGGL(w4a16_reduce_kernel, dim3(unsigned((MN + 1023) / 1024)), dim3(256), 0, s, p.part, p.y, pl.S, MN);
   return hipGetLastError();
 }
 
