@@ -9,13 +9,20 @@
 // of word packed[n][j]; zero points are bytes zeros[n][g], scales are fp16
 // scales[n][g]; x is fp16 [M][K], y is fp16 [M][N].
 //
-// Work split.  A workgroup (8 wavefronts) walks 16-row tiles of W; for one
-// tile, wavefront w covers a fixed run of up to 8 groups of K, so its share of
-// the activations (16 tokens x its K range) stays in registers for the whole
-// kernel and only W streams from HBM.  The 8 partial 16x16 results of a tile
-// meet in LDS (double-buffered, one barrier per tile) and are summed in a fixed
-// order.  Long K is cut into S splits (grid.y) whose fp32 partials a second
-// kernel adds in split order, so every result is deterministic.
+// Work split.  A workgroup (8 wavefronts, one per compute unit) walks 16-row
+// tiles of W; wavefront w always covers the same run of up to 8 groups of K,
+// so its share of the activations (16 tokens x its K range) stays in registers
+// for the whole kernel and only W streams from HBM, through a ring of a few
+// 1 KB slots per wavefront.  Each tile's scales and zero points are loaded once
+// by the whole workgroup into an LDS table, a tile ahead.  The 8 partial 16x16
+// results of a tile meet in LDS (double-buffered, one barrier per tile) and
+// are summed in a fixed order.  Long K is cut into S splits (grid.y) whose
+// fp32 partials a second kernel adds in split order, so every result is
+// deterministic.
+//
+// Activations are loaded coalesced (4 tokens x 256 B per load) and turned into
+// the MFMA operand layout through a small LDS tile by the first tile, group by
+// group, while the weight stream is already running.
 //
 // Unpacking.  With the interleaved field order, one AND-OR puts two codes into
 // the mantissas of two fp16 values: fields at bits 0-3 / 16-19 become 1024 + q
@@ -46,9 +53,7 @@ constexpr int kW4ReduceUnroll = 8;               // split partials requested tog
 
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 
-// The eight codes of one word as the B operand of a 16x16x32 MFMA (codes in
-// k order 0..7): pairs (0,1) and (4,5) as 1024 + q, pairs (2,3) and (6,7) as
-// 64 + q.
+// (w & mask) | magic as one instruction.
 __device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic) {
   uint32_t r;
   // One VOP3 instruction; the compiler would split it in two, since gfx950's
@@ -57,6 +62,9 @@ __device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t m
   return r;
 }
 
+// The eight codes of one word as the B operand of a 16x16x32 MFMA (codes in
+// k order 0..7): pairs (0,1) and (4,5) as 1024 + q, pairs (2,3) and (6,7) as
+// 64 + q.
 __device__ __forceinline__ u32x4 widen_word(uint32_t w, uint32_t m1024, uint32_t m64) {
   const uint32_t w8 = w >> 8;
   u32x4 b;
@@ -76,6 +84,7 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 // (weights): row col of the tile, same k.  D: tokens 4 * quad + i (i < 4),
 // row col.  Within a group, chunk t of lane quad is word 4 * quad + t of the
 // row, so one 16-byte load per lane brings a lane's four words of a group.
+//
 // Weight words in flight per wavefront: a ring of D slots of one group each
 // (16 rows x 64 B per slot).  Three or four 1 KB slots per wavefront (24-32 KB
 // per compute unit) stream this access pattern fastest on MI355X; deeper
