@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     FP8_TILE,
     W4A16_GROUP,
     W4A16_MAX_M,
+    W4A16_TOKENS_PER_PASS,
     AttnError,
     abi_version,
     attn_bwd,

@@ -19,7 +19,8 @@ ATTN_ERR_UNSUPPORTED = 2
 ATTN_ERR_HIP = 3
 FP8_TILE = 128
 W4A16_GROUP = 128
-W4A16_MAX_M = 16
+W4A16_MAX_M = 4096
+W4A16_TOKENS_PER_PASS = 16
 
 
 class AttnError(RuntimeError):

@@ -4,6 +4,7 @@
 #include "attn.h"
 #include "w4a16.h"
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -355,7 +356,7 @@ attn_status attn_fwd_fp8_pv8(const uint8_t* q8, const uint8_t* k8, const uint8_t
 
 size_t w4a16_work_floats(int64_t M, int64_t N, int64_t K, int64_t group) {
   if (check_w4a16(M, N, K, group) != ATTN_OK) return 0;
-  return eta::w4a16_plan(M, N, K).work_floats;
+  return eta::w4a16_plan(std::min<int64_t>(M, W4A16_TOKENS_PER_PASS), N, K).work_floats;
 }
 
 attn_status w4a16_gemm(const void* x, const uint32_t* packed, const void* scales, const uint8_t* zeros, void* y,
@@ -363,21 +364,27 @@ attn_status w4a16_gemm(const void* x, const uint32_t* packed, const void* scales
   if (attn_status s = check_w4a16(M, N, K, group)) return s;
   if (attn_status s = check_ptrs16({x, packed})) return s;
   if (!scales || !aligned(scales, 2) || !zeros || !y || !aligned(y, 2)) return ATTN_ERR_INVALID;
-  const eta::W4Plan pl = eta::w4a16_plan(M, N, K);
+  const int64_t mp = std::min<int64_t>(M, W4A16_TOKENS_PER_PASS);
+  const eta::W4Plan pl = eta::w4a16_plan(mp, N, K);  // the same plan for every pass
   if (pl.work_floats && (!work || !aligned(work, 4))) return ATTN_ERR_INVALID;
   const int cu = device_compute_units();
-  eta::W4Params p{};
-  p.x = static_cast<const uint16_t*>(x);
-  p.packed = packed;
-  p.scales = static_cast<const uint16_t*>(scales);
-  p.zeros = zeros;
-  p.y = static_cast<uint16_t*>(y);
-  p.part = pl.work_floats ? work : nullptr;
-  p.M = int(M);
-  p.N = int(N);
-  p.K = int(K);
-  p.NG = int(K / group);
-  return from_hip(eta::launch_w4a16(p, pl, cu > 0 ? cu : 256, (hipStream_t)stream));
+  // One pass per block of up to 16 tokens, in order on the caller's stream
+  // (passes reuse the workspace one after another).
+  for (int64_t m0 = 0; m0 < M; m0 += W4A16_TOKENS_PER_PASS) {
+    eta::W4Params p{};
+    p.x = static_cast<const uint16_t*>(x) + m0 * K;
+    p.packed = packed;
+    p.scales = static_cast<const uint16_t*>(scales);
+    p.zeros = zeros;
+    p.y = static_cast<uint16_t*>(y) + m0 * N;
+    p.part = pl.work_floats ? work : nullptr;
+    p.M = int(std::min<int64_t>(W4A16_TOKENS_PER_PASS, M - m0));
+    p.N = int(N);
+    p.K = int(K);
+    p.NG = int(K / group);
+    if (attn_status s = from_hip(eta::launch_w4a16(p, pl, cu > 0 ? cu : 256, (hipStream_t)stream))) return s;
+  }
+  return ATTN_OK;
 }
 
 }  // extern "C"

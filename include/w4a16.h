@@ -41,8 +41,12 @@ extern "C" {
 
 /* Codes per group (the only group size the kernels take). */
 #define W4A16_GROUP 128
-/* Largest token count M of one call (one MFMA block of tokens: decode). */
-#define W4A16_MAX_M 16
+/* Tokens per pass over W (one MFMA block of tokens).  A call with M > 16
+ * makes ceil(M / 16) passes, reading W once per pass: the kernels are built
+ * for decoding (M <= 16), where W is read exactly once. */
+#define W4A16_TOKENS_PER_PASS 16
+/* Largest token count M of one call. */
+#define W4A16_MAX_M 4096
 
 /*
  * w4a16_work_floats - fp32 workspace that w4a16_gemm needs for these sizes

@@ -147,7 +147,8 @@ def test_bwd_validation():
     (1, 16, 4096, 32 * 1 * 16),          # one tile: K cut into one split per group
     (4, 100, 1024, 8 * 4 * 100),         # seven tiles, eight groups
     (16, 4096, 128, 0),                  # one group
-    (0, 16, 128, 0), (17, 16, 128, 0), (1, 16, 100, 0),  # rejected sizes
+    (17, 16, 4096, 32 * 16 * 16),         # two passes of 16 tokens share one workspace
+    (0, 16, 128, 0), (4097, 16, 128, 0), (1, 16, 100, 0),  # rejected sizes
 ])
 def test_w4a16_work_floats(M, N, K, want):
     assert eta.w4a16_work_floats(M, N, K) == want
@@ -179,7 +180,7 @@ def w4(*, x=P16, packed=P16b, scales=P4, zeros=P4, y=P4, work=NUL, M=4, N=32, K=
     (dict(K=2**24 + 128), eta.ATTN_ERR_INVALID),
     (dict(group=64, K=256), eta.ATTN_ERR_UNSUPPORTED),
     (dict(group=0), eta.ATTN_ERR_INVALID),
-    (dict(M=17), eta.ATTN_ERR_UNSUPPORTED),
+    (dict(M=4097), eta.ATTN_ERR_UNSUPPORTED),
     (dict(work=NUL, M=1, N=16, K=4096), eta.ATTN_ERR_INVALID),          # needs a workspace
     (dict(work=ctypes.c_void_p(0x50002), M=1, N=16, K=4096), eta.ATTN_ERR_INVALID),
 ])

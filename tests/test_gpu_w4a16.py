@@ -68,6 +68,8 @@ SHAPES = [
     # (M, N, K): ragged tokens and rows, one to many groups, one to several K splits
     (1, 1, 128), (1, 16, 128), (2, 17, 256), (7, 100, 1024), (16, 33, 3072), (16, 256, 8192),
     (3, 40, 28672), (16, 1000, 4096), (5, 4096, 1152), (16, 2048, 16384),
+    # more than one pass of 16 tokens
+    (17, 100, 1024), (40, 300, 2048), (64, 1024, 28672),
 ]
 
 
