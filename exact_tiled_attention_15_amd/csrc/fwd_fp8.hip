@@ -198,6 +198,18 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
   u32x4 kreg[QK16 ? G::K_PER_THREAD : 1];
   auto kstage = [&](int t) { return smem + (t & 1) * G::K_BYTES; };
   auto vstage = [&](int t) { return smem + 2 * G::K_BYTES + (t & 1) * G::V_BYTES; };
+  // Direct-load form: this wavefront's loads are j = wave + W * jj; each
+  // lane's row and column offset within a tile are fixed, so they are
+  // computed once here and each tile only adds its first key.
+  constexpr int NJ = (G::K_LOADS + W - 1) / W;
+  int k_row[NJ], k_col[NJ];
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) {
+    const int slot = (wave + W * jj) * 64 + lane;
+    const int ch = slot % G::K_SLOTS;
+    k_row[jj] = slot / G::K_SLOTS;
+    k_col[jj] = (ch < G::CPR ? ch : 0) * 16;
+  }
   auto load_k = [&](int t) {
     const int k0 = t * BN;
     if constexpr (QK16) {
@@ -210,13 +222,15 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
       }
     } else {
       char* kb = kstage(t);
-      for (int j = wave; j < G::K_LOADS; j += W) {
-        const int slot = j * 64 + lane;
-        const int row = slot / G::K_SLOTS, ch = slot % G::K_SLOTS;
-        const int key = min(k0 + row, Nk - 1);
-        const uint8_t* src = kg + (int64_t)key * D + (ch < G::CPR ? ch : 0) * 16;
-        const unsigned base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)(kb + j * 1024);
-        load_lds16(src, __builtin_amdgcn_readfirstlane(base));
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) {
+        const int j = wave + W * jj;
+        if (j < G::K_LOADS) {  // wave-uniform
+          const int key = min(k0 + k_row[jj], Nk - 1);
+          const uint8_t* src = kg + (int64_t)key * D + k_col[jj];
+          const unsigned base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)(kb + j * 1024);
+          load_lds16(src, __builtin_amdgcn_readfirstlane(base));
+        }
       }
     }
   };
@@ -232,13 +246,20 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
       }
     }
   };
+  const int v_off_lane = 4 * v_kg * D + v_dc * 8;  // this thread's keys and columns within a tile
   auto gload_v = [&](int t) {
     if (!v_stager) return;
     const int k0 = t * BN;
+    const uint8_t* src = vg + (int64_t)k0 * D + v_off_lane;
+    if (k0 + BN <= Nk) {  // wave-uniform: the whole tile lies inside V
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = k0 + 4 * v_kg + r;
-      vreg[r] = key < Nk ? *(const u32x2*)(vg + (int64_t)key * D + v_dc * 8) : (u32x2){0u, 0u};
+      for (int r = 0; r < 4; ++r) vreg[r] = *(const u32x2*)(src + r * D);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = k0 + 4 * v_kg + r;
+        vreg[r] = key < Nk ? *(const u32x2*)(src + r * D) : (u32x2){0u, 0u};
+      }
     }
   };
   auto lstore_v = [&](int t) {
