@@ -139,6 +139,24 @@ def main():
         step = lambda: eta.attn_fwd(q, k, v, o, lse, causal, scale, stream)
         kernel = "fwd_bf16_kernel"
         launches = 1
+    elif dtype == "bf16" and cfg.get("host_kv"):
+        nb = cfg["n_blocks"]
+        blk = Nk // nb
+        q = bf(x["q"])
+        # blocks in page-locked host memory, hop order = block order
+        kh = [torch.from_numpy(np.ascontiguousarray(x["k"][:, :, i * blk:(i + 1) * blk]).view(np.int16))
+              .view(torch.bfloat16).pin_memory() for i in range(nb)]
+        vh = [torch.from_numpy(np.ascontiguousarray(x["v"][:, :, i * blk:(i + 1) * blk]).view(np.int16))
+              .view(torch.bfloat16).pin_memory() for i in range(nb)]
+        pos = [i * blk for i in range(nb)]
+        o = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((B, H, Nq), device="cuda")
+        work = torch.empty((eta.ring_work_floats(B, H, Nq, d),), device="cuda")
+        stage = torch.empty((eta.ring_stage_bytes(B, H, blk, d),), dtype=torch.uint8, device="cuda")
+        step = lambda: eta.attn_fwd_ring_host(q, kh, vh, pos, o, lse, work, stage, causal, 0, scale, stream)
+        kernel = "fwd_bf16_kernel (state epilogue) + merge_kernel, via attn_fwd_ring_host"
+        launches = 2 * nb - 1
+        transfer = host_kv_parts(args, eta, q, kh, vh, pos, o, lse, work, causal, scale, stream)
     elif dtype == "bf16" and cfg.get("ring"):
         nb = cfg["n_blocks"]
         blk = Nk // nb
@@ -192,6 +210,8 @@ def main():
         kernel = "fwd_fp8_kernel"
         launches = 1
 
+    if not cfg.get("host_kv"):
+        transfer = None
     flop = configs.workload_flops(name)
     for _ in range(args.warmup):
         step()
@@ -253,6 +273,13 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if transfer is not None:
+        transfer["total_ms"] = round(ms, 4)
+        c, g = transfer["copy_ms"], transfer["compute_ms"]
+        # share of the shorter of the two parts that ran under the other
+        transfer["hidden_frac"] = round(max(0.0, c + g - ms) / min(c, g), 4)
+        out["transfer"] = transfer
+        out["data"] += "; K/V blocks in page-locked host memory, copied to the GPU inside the timed step"
     print(json.dumps(out), flush=True)
 
 
@@ -316,6 +343,46 @@ def cpu_baseline(name, cfg, seed, x, target_s):
         "flop": flop,
         "seconds": round(elapsed, 3),
     }
+
+
+def host_kv_parts(args, eta, q, kh, vh, pos, o, lse, work, causal, scale, stream):
+    """The two parts of a host-streamed ring step timed alone: the host-to-device copies of
+    every block (into two device slots, as the step does) and the attention over the same
+    blocks already resident on the device (attn_fwd_ring)."""
+    import torch
+
+    kd = [t.cuda() for t in kh]
+    vd = [t.cuda() for t in vh]
+    slots = [torch.empty_like(kd[0]) for _ in range(4)]
+
+    def copies():
+        for i in range(len(kh)):
+            slots[2 * (i & 1)].copy_(kh[i], non_blocking=True)
+            slots[2 * (i & 1) + 1].copy_(vh[i], non_blocking=True)
+
+    def compute():
+        eta.attn_fwd_ring(q, kd, vd, pos, o, lse, work, causal, 0, scale, stream)
+
+    def timed(fn, n):
+        for _ in range(max(1, args.warmup // 2)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    n = max(3, args.steps // 2)
+    copy_ms = timed(copies, n)
+    compute_ms = timed(compute, n)
+    nbytes = 2 * sum(t.numel() * t.element_size() for t in kh)
+    del kd, vd, slots
+    torch.cuda.empty_cache()
+    return {"bytes_per_step": nbytes, "copy_ms": round(copy_ms, 4), "copy_GBps": round(nbytes / copy_ms / 1e6, 2),
+            "compute_ms": round(compute_ms, 4)}
 
 
 def bench_w4a16(args, name, cfg):

@@ -25,9 +25,11 @@ from ._lib import (  # noqa: F401
     attn_fwd_fp8_qk16,
     attn_fwd_kvblock,
     attn_fwd_ring,
+    attn_fwd_ring_host,
     attn_merge,
     bwd_work_floats,
     lib,
+    ring_stage_bytes,
     ring_work_floats,
     status_str,
     w4a16_gemm,

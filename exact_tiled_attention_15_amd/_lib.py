@@ -63,6 +63,10 @@ def lib() -> ctypes.CDLL:
     L.attn_ring_work_floats.argtypes = [i, i, i, i]
     L.attn_fwd_ring.restype = i
     L.attn_fwd_ring.argtypes = [vp, vp, vp, vp, i, vp, vp, vp, i, i, i, i, i, i, i64, f, vp]
+    L.attn_ring_stage_bytes.restype = ctypes.c_size_t
+    L.attn_ring_stage_bytes.argtypes = [i, i, i, i]
+    L.attn_fwd_ring_host.restype = i
+    L.attn_fwd_ring_host.argtypes = [vp, vp, vp, vp, i, vp, vp, vp, vp, i, i, i, i, i, i, i64, f, vp]
     for name in ("attn_fwd_fp8", "attn_fwd_fp8_qk16", "attn_fwd_fp8_pv8"):
         fn = getattr(L, name)
         fn.restype = i
@@ -221,6 +225,42 @@ def attn_fwd_ring(q, k_blks, v_blks, k_pos, o, lse, work, causal: bool, q_pos0: 
     pos = (ctypes.c_int64 * max(n, 1))(*[int(x) for x in k_pos])
     _check(lib().attn_fwd_ring(_ptr(q), kp, vp_, pos, n, _ptr(o), _ptr(lse), _ptr(work), B, H, Nq, Nkb, d,
                                int(bool(causal)), int(q_pos0), float(scale), _stream(stream)), "attn_fwd_ring")
+
+
+def ring_stage_bytes(B: int, H: int, Nk_blk: int, d: int) -> int:
+    """Size (bytes) of the device staging buffer attn_fwd_ring_host needs (two K/V slots)."""
+    return int(lib().attn_ring_stage_bytes(B, H, Nk_blk, d))
+
+
+def attn_fwd_ring_host(q, k_blks, v_blks, k_pos, o, lse, work, stage, causal: bool, q_pos0: int,
+                       scale: float, stream=None):
+    """attn_fwd_ring with the K/V blocks in host memory: k_blks[b], v_blks[b] are contiguous CPU
+    bf16 tensors [B,H,Nk_blk,d] (page-locked, e.g. pin_memory(), for the copies to overlap the
+    attention); stage is a device uint8 buffer of ring_stage_bytes(B,H,Nk_blk,d) bytes."""
+    B, H, Nq, d = q.shape
+    n = len(k_blks)
+    if len(v_blks) != n or len(k_pos) != n:
+        raise ValueError("k_blks, v_blks and k_pos must have the same length")
+    Nkb = k_blks[0].shape[2] if n else 1
+    _want(q, torch.bfloat16, (B, H, Nq, d), "q")
+    for b in range(n):
+        for name, t in ((f"k_blks[{b}]", k_blks[b]), (f"v_blks[{b}]", v_blks[b])):
+            if t.dtype != torch.bfloat16 or tuple(t.shape) != (B, H, Nkb, d):
+                raise ValueError(f"{name} must be bf16 of shape {(B, H, Nkb, d)}")
+            if t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous host tensor")
+    _want(o, torch.bfloat16, (B, H, Nq, d), "o")
+    if lse is not None:
+        _want(lse, torch.float32, (B, H, Nq), "lse")
+    _want(work, torch.float32, (ring_work_floats(B, H, Nq, d),), "work")
+    # with no block the slot size is undefined: any staging buffer will do
+    _want(stage, torch.uint8, (ring_stage_bytes(B, H, Nkb, d) if n else stage.numel(),), "stage")
+    kp = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in k_blks])
+    vp_ = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in v_blks])
+    pos = (ctypes.c_int64 * max(n, 1))(*[int(x) for x in k_pos])
+    _check(lib().attn_fwd_ring_host(_ptr(q), kp, vp_, pos, n, _ptr(o), _ptr(lse), _ptr(work), _ptr(stage), B, H,
+                                    Nq, Nkb, d, int(bool(causal)), int(q_pos0), float(scale), _stream(stream)),
+           "attn_fwd_ring_host")
 
 
 def _fwd_fp8(entry, q8, k8, v8, q_scale, k_scale, v_scale, o, lse, causal, scale, stream):

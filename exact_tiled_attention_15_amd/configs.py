@@ -28,6 +28,12 @@ WORKLOADS = {
     "bf16_causal_ring_B1_H16_N65536_R8_d128": dict(index=5, B=1, H=16, Nq=8192, Nk=65536, d=128,
                                                    dtype="bf16", causal=True, n_blocks=8,
                                                    q_pos0=57344, ring=True, oracle_rows=256),
+    # The kvblocks share with the 8 K/V blocks arriving from page-locked host memory,
+    # each block's transfer overlapped with the previous block's attention (the host link
+    # stands in for the ring's peer link).
+    "bf16_ring_host_B1_H16_Nq8192_Nk65536x8_d128": dict(index=10, B=1, H=16, Nq=8192, Nk=65536,
+                                                        d=128, dtype="bf16", causal=False,
+                                                        n_blocks=8, host_kv=True, oracle_rows=512),
     # The backward pass (dQ, dK, dV from the saved LSE) of the GPT-style causal shape; dO
     # is a seeded N(0,1) draw (sub-stream 6).
     "bwd_bf16_causal_B8_H16_N2048_d128": dict(index=6, B=8, H=16, Nq=2048, Nk=2048, d=128,

@@ -1,6 +1,8 @@
 // C ABI of libattn.so: argument validation on the host, then kernel dispatch.
-// Nothing here allocates device memory or synchronises; every check happens
-// before the first HIP call, so a rejected call has no side effect.
+// Nothing here allocates device memory or synchronises the host; every check
+// happens before the first HIP call, so a rejected call has no side effect.
+// The one HIP object the library creates itself is attn_fwd_ring_host's copy
+// stream (with its events), once per device.
 #include "attn.h"
 #include "w4a16.h"
 
@@ -8,6 +10,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "common.h"
 
@@ -143,6 +146,96 @@ attn_status check_w4a16(int64_t M, int64_t N, int64_t K, int64_t group) {
   return ATTN_OK;
 }
 
+// Arguments shared by attn_fwd_ring and attn_fwd_ring_host.
+attn_status check_ring(const void* q, const void* const* k_blks, const void* const* v_blks, const int64_t* k_pos,
+                       int n_blk, void* o, float* lse, float* work, int B, int H, int Nq, int Nk_blk, int d,
+                       int causal, int64_t q_pos0, float scale) {
+  if (n_blk < 0) return ATTN_ERR_INVALID;
+  if (attn_status s = check_shape(B, H, Nq, Nk_blk, d)) return s;
+  if (attn_status s = check_ptrs16({q, o, work})) return s;
+  if (attn_status s = check_ptrs4({lse}, true)) return s;
+  if (!std::isfinite(scale)) return ATTN_ERR_INVALID;
+  if (n_blk > 0 && (!k_blks || !v_blks || !k_pos)) return ATTN_ERR_INVALID;
+  if (causal && q_pos0 < 0) return ATTN_ERR_INVALID;
+  for (int b = 0; b < n_blk; ++b)
+    if (causal && k_pos[b] < 0) return ATTN_ERR_INVALID;
+  if (!merge_grid_ok(int64_t(B) * H * Nq, d)) return ATTN_ERR_INVALID;
+  return ATTN_OK;
+}
+
+// The hop loop of one GPU's ring share over the live blocks (with a causal
+// mask, a block whose first key comes after the shard's last row holds no
+// allowed key for any row and is skipped).  before(i, b) runs ahead of live
+// block i's launches (it returns that block's device K and V), after(i) runs
+// behind them; both return a HIP error or hipSuccess.
+template <class Before, class After>
+attn_status run_ring(const void* q, const int64_t* k_pos, int n_blk, void* o, float* lse, float* work, int B, int H,
+                     int Nq, int Nk_blk, int d, int causal, int64_t q_pos0, float scale, hipStream_t s,
+                     Before before, After after) {
+  const int64_t rows = int64_t(B) * H * Nq;
+  float* o_acc = work;
+  float* o_part = work + rows * d;
+  float* m_acc = work + 2 * rows * d;
+  float* l_acc = m_acc + rows;
+  float* m_part = l_acc + rows;
+  float* l_part = m_part + rows;
+  const int64_t last_row = q_pos0 + Nq - 1;
+  auto live = [&](int b) { return !causal || k_pos[b] <= last_row; };
+  int n_live = 0;
+  for (int b = 0; b < n_blk; ++b) n_live += live(b) ? 1 : 0;
+  if (n_live == 0)  // every row sees no key: O = 0, LSE = -inf
+    return from_hip(launch_merge_rows(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, o, lse, rows, d, s));
+  int i = 0;
+  for (int b = 0; b < n_blk; ++b) {
+    if (!live(b)) continue;
+    const void* kb = nullptr;
+    const void* vb = nullptr;
+    if (hipError_t e = before(i, b, kb, vb)) return from_hip(e);
+    if (i == 0) {  // the first live block's state becomes the accumulator
+      if (hipError_t e = launch_kvblock(q, kb, vb, o_acc, m_acc, l_acc, B, H, Nq, Nk_blk, d, causal != 0, q_pos0,
+                                        k_pos[b], scale, s))
+        return from_hip(e);
+    } else {
+      if (hipError_t e = launch_kvblock(q, kb, vb, o_part, m_part, l_part, B, H, Nq, Nk_blk, d, causal != 0,
+                                        q_pos0, k_pos[b], scale, s))
+        return from_hip(e);
+      const bool last = i == n_live - 1;
+      if (hipError_t e = launch_merge_rows(o_acc, m_acc, l_acc, o_part, m_part, l_part, last ? o : nullptr,
+                                           last ? lse : nullptr, rows, d, s))
+        return from_hip(e);
+    }
+    if (hipError_t e = after(i)) return from_hip(e);
+    ++i;
+  }
+  if (n_live == 1)  // finish the single block: merge it with the empty state
+    return from_hip(launch_merge_rows(o_acc, m_acc, l_acc, nullptr, nullptr, nullptr, o, lse, rows, d, s));
+  return ATTN_OK;
+}
+
+// Per-device copy stream and events of attn_fwd_ring_host, created on first
+// use and kept until the process ends.  The mutex serialises whole calls, so
+// the events' record/wait order is the order of the enqueued work.
+struct RingCopier {
+  std::mutex mu;
+  bool ready = false;
+  hipStream_t copy = nullptr;
+  hipEvent_t start = nullptr;
+  hipEvent_t copied[2] = {nullptr, nullptr};
+  hipEvent_t freed[2] = {nullptr, nullptr};
+};
+constexpr int kMaxDevices = 64;
+RingCopier g_copiers[kMaxDevices];
+
+hipError_t copier_init(RingCopier& c) {
+  if (c.ready) return hipSuccess;
+  if (hipError_t e = hipStreamCreateWithFlags(&c.copy, hipStreamNonBlocking)) return e;
+  hipEvent_t* evs[5] = {&c.start, &c.copied[0], &c.copied[1], &c.freed[0], &c.freed[1]};
+  for (hipEvent_t* ev : evs)
+    if (hipError_t e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) return e;
+  c.ready = true;
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -223,62 +316,75 @@ size_t attn_ring_work_floats(int B, int H, int Nq, int d) {
   return 2 * rows * size_t(d) + 4 * rows;
 }
 
+
 attn_status attn_fwd_ring(const void* q, const void* const* k_blks, const void* const* v_blks,
                           const int64_t* k_pos, int n_blk, void* o, float* lse, float* work, int B, int H,
                           int Nq, int Nk_blk, int d, int causal, int64_t q_pos0, float scale, void* stream) {
-  if (n_blk < 0) return ATTN_ERR_INVALID;
-  if (attn_status s = check_shape(B, H, Nq, Nk_blk, d)) return s;
-  if (attn_status s = check_ptrs16({q, o, work})) return s;
-  if (attn_status s = check_ptrs4({lse}, true)) return s;
-  if (!std::isfinite(scale)) return ATTN_ERR_INVALID;
-  if (n_blk > 0 && (!k_blks || !v_blks || !k_pos)) return ATTN_ERR_INVALID;
-  if (causal && q_pos0 < 0) return ATTN_ERR_INVALID;
-  for (int b = 0; b < n_blk; ++b) {
-    if (attn_status s = check_ptrs16({k_blks[b], v_blks[b]})) return s;
-    if (causal && k_pos[b] < 0) return ATTN_ERR_INVALID;
-  }
-  const int64_t rows = int64_t(B) * H * Nq;
-  if (!merge_grid_ok(rows, d)) return ATTN_ERR_INVALID;
-  float* o_acc = work;
-  float* o_part = work + rows * d;
-  float* m_acc = work + 2 * rows * d;
-  float* l_acc = m_acc + rows;
-  float* m_part = l_acc + rows;
-  float* l_part = m_part + rows;
-  const hipStream_t s = (hipStream_t)stream;
-  // With a causal mask a block whose first key comes after the shard's last
-  // row holds no allowed key for any row: skip it.
-  const int64_t last_row = q_pos0 + Nq - 1;
-  auto live = [&](int b) { return !causal || k_pos[b] <= last_row; };
-  int n_live = 0, last_live = -1;
+  if (attn_status s = check_ring(q, k_blks, v_blks, k_pos, n_blk, o, lse, work, B, H, Nq, Nk_blk, d, causal,
+                                 q_pos0, scale))
+    return s;
   for (int b = 0; b < n_blk; ++b)
-    if (live(b)) {
-      ++n_live;
-      last_live = b;
-    }
-  if (n_live == 0)  // every row sees no key: O = 0, LSE = -inf
-    return from_hip(launch_merge_rows(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, o, lse, rows, d, s));
-  bool first = true;
-  for (int b = 0; b < n_blk; ++b) {
-    if (!live(b)) continue;
-    if (first) {  // the first live block's state becomes the accumulator
-      if (hipError_t e = launch_kvblock(q, k_blks[b], v_blks[b], o_acc, m_acc, l_acc, B, H, Nq, Nk_blk, d,
-                                        causal != 0, q_pos0, k_pos[b], scale, s))
-        return from_hip(e);
-      first = false;
-      continue;
-    }
-    if (hipError_t e = launch_kvblock(q, k_blks[b], v_blks[b], o_part, m_part, l_part, B, H, Nq, Nk_blk, d,
-                                      causal != 0, q_pos0, k_pos[b], scale, s))
-      return from_hip(e);
-    const bool last = b == last_live;
-    if (hipError_t e = launch_merge_rows(o_acc, m_acc, l_acc, o_part, m_part, l_part, last ? o : nullptr,
-                                         last ? lse : nullptr, rows, d, s))
-      return from_hip(e);
+    if (attn_status s = check_ptrs16({k_blks[b], v_blks[b]})) return s;
+  auto before = [&](int, int b, const void*& kb, const void*& vb) {
+    kb = k_blks[b];
+    vb = v_blks[b];
+    return hipSuccess;
+  };
+  auto after = [](int) { return hipSuccess; };
+  return run_ring(q, k_pos, n_blk, o, lse, work, B, H, Nq, Nk_blk, d, causal, q_pos0, scale, (hipStream_t)stream,
+                  before, after);
+}
+
+size_t attn_ring_stage_bytes(int B, int H, int Nk_blk, int d) {
+  if (B <= 0 || H <= 0 || Nk_blk <= 0 || d <= 0) return 0;
+  return 4 * size_t(B) * size_t(H) * size_t(Nk_blk) * size_t(d) * 2;  // two slots of K and V, bf16
+}
+
+attn_status attn_fwd_ring_host(const void* q, const void* const* k_blks, const void* const* v_blks,
+                               const int64_t* k_pos, int n_blk, void* o, float* lse, float* work, void* stage,
+                               int B, int H, int Nq, int Nk_blk, int d, int causal, int64_t q_pos0, float scale,
+                               void* stream) {
+  if (attn_status s = check_ring(q, k_blks, v_blks, k_pos, n_blk, o, lse, work, B, H, Nq, Nk_blk, d, causal,
+                                 q_pos0, scale))
+    return s;
+  for (int b = 0; b < n_blk; ++b)
+    if (!k_blks[b] || !v_blks[b]) return ATTN_ERR_INVALID;
+  if (attn_status s = check_ptrs16({stage})) return s;
+  const size_t stage_bytes = attn_ring_stage_bytes(B, H, Nk_blk, d);
+  const size_t work_bytes = attn_ring_work_floats(B, H, Nq, d) * sizeof(float);
+  {
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(stage), w0 = reinterpret_cast<uintptr_t>(work);
+    if (s0 < w0 + work_bytes && w0 < s0 + stage_bytes) return ATTN_ERR_INVALID;
   }
-  if (n_live == 1)  // finish the single block: merge it with the empty state
-    return from_hip(launch_merge_rows(o_acc, m_acc, l_acc, nullptr, nullptr, nullptr, o, lse, rows, d, s));
-  return ATTN_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_HIP;
+  RingCopier& c = g_copiers[dev];
+  std::lock_guard<std::mutex> lock(c.mu);
+  if (copier_init(c) != hipSuccess) return ATTN_ERR_HIP;
+  const hipStream_t s = (hipStream_t)stream;
+  const size_t blk_bytes = stage_bytes / 4;
+  char* slots = static_cast<char*>(stage);
+  // The first copy waits for the caller's earlier work on `stream` (which may
+  // still read the staging buffer).
+  if (hipEventRecord(c.start, s) != hipSuccess || hipStreamWaitEvent(c.copy, c.start, 0) != hipSuccess)
+    return ATTN_ERR_HIP;
+  auto before = [&](int i, int b, const void*& kb, const void*& vb) -> hipError_t {
+    const int slot = i & 1;
+    char* kd = slots + size_t(slot) * 2 * blk_bytes;
+    char* vd = kd + blk_bytes;
+    // live block i - 2 read this slot: its attention must have finished
+    if (i >= 2)
+      if (hipError_t e = hipStreamWaitEvent(c.copy, c.freed[slot], 0)) return e;
+    if (hipError_t e = hipMemcpyAsync(kd, k_blks[b], blk_bytes, hipMemcpyHostToDevice, c.copy)) return e;
+    if (hipError_t e = hipMemcpyAsync(vd, v_blks[b], blk_bytes, hipMemcpyHostToDevice, c.copy)) return e;
+    if (hipError_t e = hipEventRecord(c.copied[slot], c.copy)) return e;
+    if (hipError_t e = hipStreamWaitEvent(s, c.copied[slot], 0)) return e;
+    kb = kd;
+    vb = vd;
+    return hipSuccess;
+  };
+  auto after = [&](int i) { return hipEventRecord(c.freed[i & 1], s); };
+  return run_ring(q, k_pos, n_blk, o, lse, work, B, H, Nq, Nk_blk, d, causal, q_pos0, scale, s, before, after);
 }
 
 size_t attn_bwd_work_floats(int B, int H, int Nq) {

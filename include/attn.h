@@ -189,6 +189,41 @@ attn_status attn_fwd_ring(const void* q, const void* const* k_blks, const void* 
                           float scale, void* stream);
 
 /*
+ * attn_fwd_ring_host - attn_fwd_ring with the K/V blocks arriving from HOST
+ * memory, the block transfer overlapped with the attention of the previous
+ * block ("Sequence parallelism and ring attention", "Deep dive": the K/V
+ * exchange of the ring runs under the computation, so it adds little wall
+ * time).  On one GPU the host link stands in for the ring's peer link.
+ *   k_blks, v_blks   HOST arrays of n_blk HOST pointers, each block bf16
+ *                    [B,H,Nk_blk,d] in host memory.  Page-locked memory
+ *                    (hipHostMalloc) is needed for the copies to run
+ *                    asynchronously; pageable memory gives the same result
+ *                    with the copies serialised against the host thread.
+ *   stage   device buffer of attn_ring_stage_bytes(B,H,Nk_blk,d) bytes,
+ *           16-byte aligned, owned by the caller: two slots, each one
+ *           block's K then V.  Contents on return are unspecified.
+ *   other arguments as attn_fwd_ring.
+ * Live block i (blocks skipped by the causal rule are neither copied nor
+ * computed) is copied into slot i % 2 on a copy stream that the library
+ * keeps per device; its attention runs on `stream` once the copy is done,
+ * and the copy of live block i + 2 waits until that attention has finished
+ * reading the slot.  The first copy also waits for the work enqueued on
+ * `stream` before the call.  All of the call's work, copies included, is
+ * complete once `stream` reaches the point of the call's return; the host
+ * blocks must stay valid and unchanged until then.  The result is
+ * bit-identical to attn_fwd_ring on the same blocks resident on the device.
+ * Calls from several host threads are serialised inside the library.
+ * Errors: as attn_fwd_ring (a NULL block pointer is ATTN_ERR_INVALID), plus
+ * ATTN_ERR_INVALID for a NULL or misaligned `stage`, or one that overlaps
+ * `work`; ATTN_ERR_HIP if the copy stream or a copy fails.
+ */
+size_t attn_ring_stage_bytes(int B, int H, int Nk_blk, int d);
+attn_status attn_fwd_ring_host(const void* q, const void* const* k_blks, const void* const* v_blks,
+                               const int64_t* k_pos, int n_blk, void* o, float* lse, float* work,
+                               void* stage, int B, int H, int Nq, int Nk_blk, int d, int causal,
+                               int64_t q_pos0, float scale, void* stream);
+
+/*
  * attn_fwd_fp8 - attention on block-quantized OCP FP8 E4M3 ("e4m3fn") inputs
  * ("Scaling FlashAttention, multi-GPU training and weight quantization",
  * itimpress, section 1, FP8 bullet: a separate scale per small tile).

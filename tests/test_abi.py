@@ -125,6 +125,31 @@ def test_ring_validation():
     assert ring(scale=float("nan")) == eta.ATTN_ERR_INVALID
 
 
+def test_ring_host_validation():
+    """attn_fwd_ring_host rejects bad arguments before any HIP call."""
+    L = eta.lib()
+    assert L.attn_ring_stage_bytes(1, 2, 8, 64) == 4 * 2 * 8 * 64 * 2  # two slots of K and V, bf16
+    assert L.attn_ring_stage_bytes(1, 2, 0, 64) == 0
+    ks = (ctypes.c_void_p * 2)(0x100000, 0x200001)  # host blocks need no alignment
+    vs = (ctypes.c_void_p * 2)(0x300000, 0x400000)
+    nulls = (ctypes.c_void_p * 2)(0x100000, 0)
+    pos = (ctypes.c_int64 * 2)(0, 8)
+    work_bytes = L.attn_ring_work_floats(1, 1, 8, 64) * 4
+    inside_work = ctypes.c_void_p(0x30000 + (work_bytes // 2 // 16) * 16)
+    ring = lambda n=2, k=ks, v=vs, w=P16c, st=P16d, causal=1, qp=8, d=64: L.attn_fwd_ring_host(
+        P16, k, v, pos, n, P16b, NUL, w, st, 1, 1, 8, 8, d, causal, qp, 0.1, None)
+    assert ring(n=-1) == eta.ATTN_ERR_INVALID
+    assert ring(k=None) == eta.ATTN_ERR_INVALID          # NULL array with blocks
+    assert ring(v=nulls) == eta.ATTN_ERR_INVALID         # NULL host block
+    assert ring(st=NUL) == eta.ATTN_ERR_INVALID          # no staging buffer
+    assert ring(st=MIS) == eta.ATTN_ERR_INVALID          # misaligned staging buffer
+    assert ring(st=P16c) == eta.ATTN_ERR_INVALID         # staging buffer is the workspace
+    assert ring(st=inside_work) == eta.ATTN_ERR_INVALID  # ... or overlaps it
+    assert ring(w=NUL) == eta.ATTN_ERR_INVALID
+    assert ring(qp=-1) == eta.ATTN_ERR_INVALID
+    assert ring(d=96) == eta.ATTN_ERR_UNSUPPORTED
+
+
 def test_bwd_validation():
     """attn_bwd rejects bad arguments before any launch."""
     L = eta.lib()
