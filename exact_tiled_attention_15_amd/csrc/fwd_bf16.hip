@@ -99,18 +99,8 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
   const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
   const int wtiles = (qw0 < Nq && wkend > 0) ? min(ntiles, (wkend + BN - 1) / BN) : 0;
 
-  // Q fragment (B operand of S^T = K Q^T): row my_q, d = kk*16 + g*8 .. +8.
-  bf16x8 qf[D / 16];
-  {
-    const bool ok = my_q < Nq;
-    const u32x4* src = (const u32x4*)(qg + (int64_t)(ok ? my_q : 0) * D + g * 8);
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      u32x4 x = ok ? src[kk * 2] : (u32x4){0u, 0u, 0u, 0u};
-      x = (x & p.q_and) ^ p.q_xor;
-      qf[kk] = __builtin_bit_cast(bf16x8, x);
-    }
-  }
+
+  bf16x8 qf[D / 16];  // Q fragments, loaded in the prologue below
 
   // ---- staging.  K: direct global -> LDS loads; each wave-wide load fills 64
   // consecutive 16-byte slots of the padded tile (slot s = row s / K_SLOTS,
@@ -149,20 +139,19 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
       }
     }
   };
-  const int v_off_lane = 4 * v_kg * D + v_dc * 8;  // this thread's keys and columns within a tile
+  // V keys past Nk read the last row instead: their probabilities are exactly
+  // 0, so every load is unconditional (no load waits for another).
+  const uint16_t* __restrict__ v_col = vg + v_dc * 8;
   auto gload_v = [&](int t) {
     if (!v_stager) return;
-    const int k0 = t * BN;
-    const uint16_t* src = vg + (int64_t)k0 * D + v_off_lane;
-    if (k0 + BN <= Nk) {  // wave-uniform: the whole tile lies inside V
+    const int kfirst = t * BN + 4 * v_kg;
+    if (t * BN + BN <= Nk) {  // workgroup-uniform: the whole tile lies inside V
+      const uint16_t* src = v_col + (int64_t)kfirst * D;
 #pragma unroll
       for (int r = 0; r < 4; ++r) vreg[r] = *(const u32x4*)(src + r * D);
     } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = k0 + 4 * v_kg + r;
-        vreg[r] = key < Nk ? *(const u32x4*)(src + r * D) : (u32x4){0u, 0u, 0u, 0u};
-      }
+      for (int r = 0; r < 4; ++r) vreg[r] = *(const u32x4*)(v_col + (int64_t)min(kfirst + r, Nk - 1) * D);
     }
   };
   auto lstore_v = [&](int t) {
@@ -283,11 +272,28 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
 
   // ---- tile loop: stage t%2 holds K(t) and V(t); tile t+1 is in flight
   // while tile t is computed.
+  // Prologue: the first K/V tile's loads go out first, then Q's, so the
+  // transfers overlap.  Q fragment (B operand of S^T = K Q^T): row my_q,
+  // d = kk*16 + g*8 .. +8; rows past Nq load the last row (unconditionally,
+  // so no load waits for another) and are zeroed.
   if (ntiles > 0) {
     load_k(0);
     gload_v(0);
-    lstore_v(0);
   }
+  {
+    const bool ok = my_q < Nq;
+    const u32x4* src = (const u32x4*)(qg + (int64_t)min(my_q, Nq - 1) * D + g * 8);
+    u32x4 raw[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) raw[kk] = src[kk * 2];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      u32x4 x = (raw[kk] & p.q_and) ^ p.q_xor;
+      if (!ok) x = (u32x4){0u, 0u, 0u, 0u};
+      qf[kk] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+  if (ntiles > 0) lstore_v(0);
   publish();
   for (int t = 0; t < ntiles; ++t) {
     const bool more = t + 1 < ntiles;
