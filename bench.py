@@ -96,7 +96,7 @@ def cpu_model():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: this benchmark measures one GPU only (asked for --gpus {args.gpus}); "
               "the path shards by (batch, head) and by ring hops, which no run here exercises.", file=sys.stderr)
         sys.exit(2)
 
