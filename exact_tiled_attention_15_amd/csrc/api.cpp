@@ -95,6 +95,31 @@ hipError_t launch_kvblock(const void* q, const void* k_blk, const void* v_blk, f
   return eta::launch_fwd_bf16(p, d, causal, eta::kEpiState, stream);
 }
 
+// Attention of q against one K/V block merged straight into the accumulator
+// (o_acc, m_acc, l_acc) by the kernel's epilogue; with o_final / lse_final the
+// merged result is also written as bf16 O and LSE (arguments already
+// validated).  Same result as launch_kvblock followed by launch_merge_rows,
+// without the block state's round trip through memory.
+hipError_t launch_kvblock_merge(const void* q, const void* k_blk, const void* v_blk, float* o_acc, float* m_acc,
+                                float* l_acc, void* o_final, float* lse_final, int B, int H, int Nq, int Nk_blk,
+                                int d, bool causal, int64_t q_pos0, int64_t k_pos0, float scale,
+                                hipStream_t stream) {
+  FwdParams p = base_params(B, H, Nq, Nk_blk, scale);
+  int64_t diag = q_pos0 - k_pos0;
+  if (diag > Nk_blk) diag = Nk_blk;
+  if (diag < -int64_t(Nq)) diag = -int64_t(Nq);
+  p.diag = int(diag);
+  p.q = q;
+  p.k = k_blk;
+  p.v = v_blk;
+  p.o = o_acc;
+  p.m_out = m_acc;
+  p.l_out = l_acc;
+  p.o_final = o_final;
+  p.lse = lse_final;
+  return eta::launch_fwd_bf16(p, d, causal, eta::kEpiMerge, stream);
+}
+
 // Merge (o_part, m_part, l_part) into the accumulator (arguments already
 // validated).  Inside the library a null accumulator or part stands for the
 // empty state.
@@ -174,11 +199,8 @@ attn_status run_ring(const void* q, const int64_t* k_pos, int n_blk, void* o, fl
                      Before before, After after) {
   const int64_t rows = int64_t(B) * H * Nq;
   float* o_acc = work;
-  float* o_part = work + rows * d;
-  float* m_acc = work + 2 * rows * d;
+  float* m_acc = work + rows * d;
   float* l_acc = m_acc + rows;
-  float* m_part = l_acc + rows;
-  float* l_part = m_part + rows;
   const int64_t last_row = q_pos0 + Nq - 1;
   auto live = [&](int b) { return !causal || k_pos[b] <= last_row; };
   int n_live = 0;
@@ -195,13 +217,11 @@ attn_status run_ring(const void* q, const int64_t* k_pos, int n_blk, void* o, fl
       if (hipError_t e = launch_kvblock(q, kb, vb, o_acc, m_acc, l_acc, B, H, Nq, Nk_blk, d, causal != 0, q_pos0,
                                         k_pos[b], scale, s))
         return from_hip(e);
-    } else {
-      if (hipError_t e = launch_kvblock(q, kb, vb, o_part, m_part, l_part, B, H, Nq, Nk_blk, d, causal != 0,
-                                        q_pos0, k_pos[b], scale, s))
-        return from_hip(e);
+    } else {  // later blocks merge into it in the attention kernel's epilogue
       const bool last = i == n_live - 1;
-      if (hipError_t e = launch_merge_rows(o_acc, m_acc, l_acc, o_part, m_part, l_part, last ? o : nullptr,
-                                           last ? lse : nullptr, rows, d, s))
+      if (hipError_t e = launch_kvblock_merge(q, kb, vb, o_acc, m_acc, l_acc, last ? o : nullptr,
+                                              last ? lse : nullptr, B, H, Nq, Nk_blk, d, causal != 0, q_pos0,
+                                              k_pos[b], scale, s))
         return from_hip(e);
     }
     if (hipError_t e = after(i)) return from_hip(e);
@@ -313,7 +333,7 @@ attn_status attn_merge(float* o_acc, float* m_acc, float* l_acc, const float* o_
 size_t attn_ring_work_floats(int B, int H, int Nq, int d) {
   if (B <= 0 || H <= 0 || Nq <= 0 || d <= 0) return 0;
   const size_t rows = size_t(B) * size_t(H) * size_t(Nq);
-  return 2 * rows * size_t(d) + 4 * rows;
+  return rows * size_t(d) + 2 * rows;  // the accumulated O, m and l
 }
 
 

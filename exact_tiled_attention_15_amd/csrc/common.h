@@ -38,6 +38,8 @@ enum Epilogue : int {
   kEpiFinalBf16 = 0,  // O normalised, bf16; LSE (optional)
   kEpiState = 1,      // O normalised fp32, m (natural units), l
   kEpiFinalF32 = 2,   // O normalised, fp32; LSE (optional)
+  kEpiMerge = 3,      // block state merged in place into the fp32 accumulator
+                      // (o, m_out, l_out); o_final (bf16) and lse optional
 };
 
 // Parameters of the bf16 / fp8 forward kernels (one (b,h) slice per
@@ -51,8 +53,9 @@ struct FwdParams {
   const float* v_scale;  // fp8 only
   void* o;
   float* lse;    // final epilogues; may be null
-  float* m_out;  // state epilogue
-  float* l_out;  // state epilogue
+  float* m_out;  // state and merge epilogues
+  float* l_out;  // state and merge epilogues
+  void* o_final; // merge epilogue: bf16 copy of the merged O, may be null
   int Nq, Nk;
   int BH;        // B * H
   int nqb;       // query blocks per (b,h) slice: ceil(Nq / rows per workgroup), set by the launcher

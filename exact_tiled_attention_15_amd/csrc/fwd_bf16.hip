@@ -329,6 +329,41 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
         }
       if (p.lse && g == 0)
         p.lse[row] = l_tot > 0.f ? m_run * p.scale_abs + __log2f(l_tot) * 0.69314718055994530942f : -INFINITY;
+    } else if (EPI == kEpiMerge) {
+      // Online-softmax merge with the accumulated state of this row ("Sequence
+      // parallelism and ring attention", "Technical insight"): M = max(m_acc,
+      // m_blk), w_x = l_x e^(m_x - M), O = (w_acc O_acc + w_blk O_blk) / (w_acc +
+      // w_blk).  The empty state (m = -inf, l = 0) is the identity.  Both lanes
+      // of a row read m_acc / l_acc in the same instruction before lane g = 0
+      // rewrites them.
+      float* oa = (float*)p.o + row * D;
+      const float mb = l_tot > 0.f ? m_run * p.scale_abs : -INFINITY;
+      const float ma = p.m_out[row], la = p.l_out[row];
+      const float M = fmaxf(ma, mb);
+      float wa = 0.f, wb = 0.f;
+      if (M != -INFINITY) {
+        if (ma != -INFINITY) wa = la * expf(ma - M);
+        if (mb != -INFINITY) wb = l_tot * expf(mb - M);
+      }
+      const float l = wa + wb;
+      const float il = l > 0.f ? 1.f / l : 0.f;
+      const float ca = wa * il, cb = wb * inv * il;  // the block's O is oacc / l_tot
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int col = 32 * db + 8 * r + 4 * g;
+          const f32x4 a = wa > 0.f ? *(const f32x4*)(oa + col) : (f32x4){0.f, 0.f, 0.f, 0.f};
+          const f32x4 b = {oacc[db][4 * r], oacc[db][4 * r + 1], oacc[db][4 * r + 2], oacc[db][4 * r + 3]};
+          const f32x4 v = ca * a + cb * b;
+          *(f32x4*)(oa + col) = v;
+          if (p.o_final) *(bf16x4*)((uint16_t*)p.o_final + row * D + col) = __builtin_convertvector(v, bf16x4);
+        }
+      if (g == 0) {
+        p.m_out[row] = l > 0.f ? M : -INFINITY;
+        p.l_out[row] = l;
+        if (p.lse) p.lse[row] = l > 0.f ? M + logf(l) : -INFINITY;
+      }
     } else {
       float* og = (float*)p.o + row * D;
 #pragma unroll
@@ -369,9 +404,11 @@ hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, int epi, hipS
   if (d == 128) {
     if (epi == kEpiFinalBf16) return launch_d<128, kEpiFinalBf16>(p, causal, s);
     if (epi == kEpiState) return launch_d<128, kEpiState>(p, causal, s);
+    if (epi == kEpiMerge) return launch_d<128, kEpiMerge>(p, causal, s);
   } else if (d == 64) {
     if (epi == kEpiFinalBf16) return launch_d<64, kEpiFinalBf16>(p, causal, s);
     if (epi == kEpiState) return launch_d<64, kEpiState>(p, causal, s);
+    if (epi == kEpiMerge) return launch_d<64, kEpiMerge>(p, causal, s);
   }
   return hipErrorInvalidValue;
 }

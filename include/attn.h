@@ -163,15 +163,18 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
  * parallelism and ring attention", "Deep dive" and "Technical insight"):
  * the local query shard against the K/V blocks that the ring's hops deliver,
  * in hop order, each block's partial state (as attn_fwd_kvblock) folded into
- * a running state (as attn_merge), then the final bf16 O and LSE.
+ * a running state (as attn_merge; after the first block the fold happens in
+ * the attention kernel's epilogue, so block states never round-trip through
+ * memory), then the final bf16 O and LSE.
  *   q       bf16 [B,H,Nq,d], query row i at global position q_pos0 + i
  *   k_blks, v_blks   HOST arrays of n_blk device pointers, each block
  *                    bf16 [B,H,Nk_blk,d]; block b's key j sits at global
  *                    position k_pos[b] + j (k_pos: HOST array of n_blk)
  *   o       bf16 [B,H,Nq,d]      lse  fp32 [B,H,Nq] natural log, or NULL
  *   work    device fp32 workspace of attn_ring_work_floats(B,H,Nq,d)
- *           floats, 16-byte aligned, owned by the caller; its contents on
- *           return are unspecified.  It must not overlap any other argument.
+ *           floats (B*H*Nq*(d+2): the running O, m and l), 16-byte aligned,
+ *           owned by the caller; its contents on return are unspecified.  It
+ *           must not overlap any other argument.
  * With `causal` set, key position kp is allowed for query position qp iff
  * kp <= qp; a block whose first key lies after the shard's last row holds no
  * allowed key and is skipped without a launch.  n_blk = 0, or every block

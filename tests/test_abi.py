@@ -102,7 +102,7 @@ def test_kvblock_and_merge_validation():
 def test_ring_validation():
     """attn_fwd_ring rejects bad arguments before any launch (fake pointers are never touched)."""
     L = eta.lib()
-    assert L.attn_ring_work_floats(1, 2, 8, 64) == 2 * 16 * 64 + 4 * 16
+    assert L.attn_ring_work_floats(1, 2, 8, 64) == 16 * 64 + 2 * 16  # accumulated O, m, l
     assert L.attn_ring_work_floats(0, 2, 8, 64) == 0
     ks = (ctypes.c_void_p * 2)(0x100000, 0x200000)
     vs = (ctypes.c_void_p * 2)(0x300000, 0x400000)
