@@ -6,7 +6,11 @@ One step = one pass of the hot path over one batch of synthetic input:
   * n_blocks x attn_fwd_kvblock plus the merges (block-streamed workload).
 W untimed warm-up steps, then K steps back to back on one stream, bracketed
 by HIP events recorded on that stream (torch.cuda.Event on the stream the
-kernels are launched on) and device synchronisation.  Inputs are resident in
+kernels are launched on) and device synchronisation.  Without --warmup the
+warm-up runs for at least 0.3 s and 10 steps: an idle MI355X needs about
+0.1-0.2 s of load to leave its low clocks, and a 10-step warm-up of the
+causal B8 H16 N2048 workload (2 ms) measures ~700 instead of ~850 TFLOP/s.
+The JSON line reports the warm-up step count actually run.  Inputs are resident in
 HBM before the timed region starts.  Prints one JSON line.
 
 The default workload is the causal bf16 B=8 H=16 N=2048 d=128 attention
@@ -73,13 +77,38 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: as many as take WARMUP_SECONDS, at least 10)")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain copy kernel of known size (HBM counter calibration)")
     return ap.parse_args()
+
+
+WARMUP_SECONDS = 0.3
+
+
+def warm_up(step, warmup):
+    """Run the untimed warm-up; returns the number of steps run.  `warmup`
+    steps when given; otherwise at least 10 steps and WARMUP_SECONDS of them
+    (the host waits for the GPU every 8 steps, so the time is the GPU's)."""
+    import torch
+
+    if warmup is not None:
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        return warmup
+    n, t0 = 0, time.perf_counter()
+    while n < 10 or time.perf_counter() - t0 < WARMUP_SECONDS:
+        step()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
 
 
 def cpu_model():
@@ -213,9 +242,7 @@ def main():
     if not cfg.get("host_kv"):
         transfer = None
     flop = configs.workload_flops(name)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warmup = warm_up(step, args.warmup)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
     e0.record(stream)
@@ -259,7 +286,7 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -364,9 +391,7 @@ def host_kv_parts(args, eta, q, kh, vh, pos, o, lse, work, causal, scale, stream
         eta.attn_fwd_ring(q, kd, vd, pos, o, lse, work, causal, 0, scale, stream)
 
     def timed(fn, n):
-        for _ in range(max(1, args.warmup // 2)):
-            fn()
-        torch.cuda.synchronize()
+        warm_up(fn, None if args.warmup is None else max(1, args.warmup // 2))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(n):
@@ -412,9 +437,7 @@ def bench_w4a16(args, name, cfg):
         state["i"] += 1
         eta.w4a16_gemm(x, p, sc, z, y, work, G, stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warmup = warm_up(step, args.warmup)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
     e0.record(stream)
@@ -452,7 +475,7 @@ def bench_w4a16(args, name, cfg):
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
