@@ -24,6 +24,15 @@ COMMON_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
+# Kernels whose matrix accumulators do not all fit in the architectural VGPRs:
+# without this option the compiler keeps MFMA results in AGPRs and copies the
+# live accumulators out and back around every other product (about 190
+# v_accvgpr moves per key tile in the dK/dV kernel); with it the products
+# accumulate in VGPRs directly and the long-lived sums alone sit in AGPRs.
+EXTRA_FLAGS = {
+    "bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "fwd_f32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _run(cmd):
@@ -43,7 +52,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".", "_") + ".o")
         objs.append(obj)
-        cmds.append([HIPCC, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC, *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 4)) as ex:
         for msg in ex.map(_run, cmds):
             if verbose and msg.strip():

@@ -28,7 +28,9 @@
 //                     query-permuted.
 // Probabilities and dS are rounded to bf16 for the products, accumulations are
 // fp32.  Masked (query, key) pairs get p = 0 by selection, so any finite
-// scale works.  Keys and queries beyond the tensor ends are zero-filled.
+// scale works.  Staging loads past the tensor ends read the last row instead
+// (unconditional loads, so none waits for another); every (query, key) pair
+// they form is masked, so its P and dS are exactly 0.
 #include "common.h"
 
 namespace eta {
@@ -109,12 +111,18 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_kernel(BwdParams p, int nqb) {
   bf16x8 qf[D / 16], dof[D / 16];
   const bool row_ok = my_q < Nq;
   {
-    const int64_t rq = (int64_t)(row_ok ? my_q : 0) * D + g * 8;
+    const int64_t rq = (int64_t)min(my_q, Nq - 1) * D + g * 8;
+    u32x4 rawq[D / 16], rawd[D / 16];
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      qf[kk] = __builtin_bit_cast(bf16x8, row_ok ? *(const u32x4*)(qg + rq + kk * 16) : z);
-      dof[kk] = __builtin_bit_cast(bf16x8, row_ok ? *(const u32x4*)(dog + rq + kk * 16) : z);
+      rawq[kk] = *(const u32x4*)(qg + rq + kk * 16);
+      rawd[kk] = *(const u32x4*)(dog + rq + kk * 16);
+    }
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      qf[kk] = __builtin_bit_cast(bf16x8, row_ok ? rawq[kk] : z);
+      dof[kk] = __builtin_bit_cast(bf16x8, row_ok ? rawd[kk] : z);
     }
   }
   const int64_t grow = (int64_t)bh * Nq + my_q;
@@ -138,8 +146,8 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_kernel(BwdParams p, int nqb) {
     const uint16_t* src = st == 0 ? kg : vg;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int key = t * G::BN + 4 * s_kg + r;
-      sreg[r] = key < Nk ? *(const u32x4*)(src + (int64_t)key * D + s_dc * 8) : (u32x4){0u, 0u, 0u, 0u};
+      const int key = min(t * G::BN + 4 * s_kg + r, Nk - 1);
+      sreg[r] = *(const u32x4*)(src + (int64_t)key * D + s_dc * 8);
     }
   };
   auto lstore = [&](int t) {
@@ -252,12 +260,18 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) 
   bf16x8 kf[D / 16], vf[D / 16];
   const bool key_ok = my_k < Nk;
   {
-    const int64_t rk = (int64_t)(key_ok ? my_k : 0) * D + g * 8;
+    const int64_t rk = (int64_t)min(my_k, Nk - 1) * D + g * 8;
+    u32x4 rawk[D / 16], rawv[D / 16];
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      kf[kk] = __builtin_bit_cast(bf16x8, key_ok ? *(const u32x4*)(kg + rk + kk * 16) : z);
-      vf[kk] = __builtin_bit_cast(bf16x8, key_ok ? *(const u32x4*)(vg + rk + kk * 16) : z);
+      rawk[kk] = *(const u32x4*)(kg + rk + kk * 16);
+      rawv[kk] = *(const u32x4*)(vg + rk + kk * 16);
+    }
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      kf[kk] = __builtin_bit_cast(bf16x8, key_ok ? rawk[kk] : z);
+      vf[kk] = __builtin_bit_cast(bf16x8, key_ok ? rawv[kk] : z);
     }
   }
   const float c = p.c;
@@ -271,26 +285,26 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) 
   const int s_qg = tid % G::QG, s_dc = tid / G::QG;
   u32x4 qreg[4], dreg[4];
   float sval = 0.f;
+  const float* __restrict__ sbase = (tid < G::BM ? lseg : dltg) + (tid % G::BM);
+  const float* sptr = sbase;
   auto stage_base = [&](int t) { return smem + (t & 1) * G::STAGE; };
   auto gload = [&](int t) {
     if (stager) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int q = t * G::BM + 4 * s_qg + r;
-        const bool ok = q < Nq;
-        const int64_t off = (int64_t)(ok ? q : 0) * D + s_dc * 8;
-        qreg[r] = ok ? *(const u32x4*)(qg + off) : (u32x4){0u, 0u, 0u, 0u};
-        dreg[r] = ok ? *(const u32x4*)(dog + off) : (u32x4){0u, 0u, 0u, 0u};
+        const int64_t off = (int64_t)min(t * G::BM + 4 * s_qg + r, Nq - 1) * D + s_dc * 8;
+        qreg[r] = *(const u32x4*)(qg + off);
+        dreg[r] = *(const u32x4*)(dog + off);
       }
     }
-    if (tid < 2 * G::BM) {
-      const int q = t * G::BM + (tid % G::BM);
-      if (tid < G::BM) {
-        const float l = q < Nq ? lseg[q] : -INFINITY;
-        sval = l == -INFINITY ? 0.f : l * kLog2e;  // rows without keys are masked anyway
-      } else {
-        sval = q < Nq ? dltg[q] : 0.f;
-      }
+    if (tid < 2 * G::BM) {  // raw LSE or D; converted when staged
+      // Full tiles read through a pointer carried across the tile loop, so
+      // its registers are never recycled while the load is in flight (that
+      // would cost a wait for every outstanding load); the last, ragged tile
+      // clamps its row.
+      const int q0t = t * G::BM;
+      if (q0t + G::BM <= Nq) sval = *(sptr + q0t);
+      else sval = sbase[min(q0t + (tid % G::BM), Nq - 1) - (tid % G::BM)];
     }
   };
   auto lstore = [&](int t) {
@@ -301,7 +315,11 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) 
       store_vt(b + 2 * G::R_BYTES, G::VTP, 8 * s_dc, s_qg, qreg);
       store_vt(b + 2 * G::R_BYTES + G::T_BYTES, G::VTP, 8 * s_dc, s_qg, dreg);
     }
-    if (tid < 2 * G::BM) ((float*)(b + 2 * G::R_BYTES + 2 * G::T_BYTES))[tid] = sval;
+    if (tid < 2 * G::BM) {
+      // LSE in base 2 (rows without keys, LSE = -inf, are masked anyway), or D
+      const float v = tid < G::BM ? (sval == -INFINITY ? 0.f : sval * kLog2e) : sval;
+      ((float*)(b + 2 * G::R_BYTES + 2 * G::T_BYTES))[tid] = v;
+    }
   };
 
   const int r_off = r32 * G::KS + g * 16;
@@ -311,6 +329,9 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) 
     gload(t0);
     lstore(t0);
   }
+  // All loads so far (the stationary K and V too) have landed: said
+  // explicitly, so that no wait for them is left inside the tile loop.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int t = t0; t < ntiles; ++t) {
     const bool more = t + 1 < ntiles;
