@@ -138,7 +138,9 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_kernel(BwdParams p, int nqb) {
 
   // Staging: thread (tensor, dc, kgrp) holds keys 4*kgrp .. +3, columns 8*dc .. +7.
   const int st = tid / G::STAGERS;  // 0: K, 1: V, 2+: idle
-  const int su = tid - st * G::STAGERS, s_kg = su % G::KG, s_dc = su / G::KG;
+  // The column chunk is rotated by the key group so that the 16 lanes of one
+  // row store (rows 4 apart) cover all 16-byte bank groups instead of 4.
+  const int su = tid - st * G::STAGERS, s_kg = su % G::KG, s_dc = (su / G::KG + s_kg) % (D / 8);
   u32x4 sreg[4];
   auto stage_base = [&](int t) { return smem + (t & 1) * G::STAGE; };
   auto gload = [&](int t) {
@@ -282,7 +284,9 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) 
   // Staging: thread (dc, qgrp) holds queries 4*qgrp .. +3, columns 8*dc .. +7
   // of Q and of dO; threads 0 .. BM-1 also fetch LSE2, BM .. 2BM-1 fetch D.
   const bool stager = tid < G::STAGERS;
-  const int s_qg = tid % G::QG, s_dc = tid / G::QG;
+  // Column chunk rotated by the query group: the 16 lanes of one row store
+  // (rows 4 apart) then cover all 16-byte bank groups instead of 4.
+  const int s_qg = tid % G::QG, s_dc = (tid / G::QG + s_qg) % (D / 8);
   u32x4 qreg[4], dreg[4];
   float sval = 0.f;
   const float* __restrict__ sbase = (tid < G::BM ? lseg : dltg) + (tid % G::BM);
