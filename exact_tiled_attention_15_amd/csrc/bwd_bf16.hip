@@ -370,24 +370,36 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) 
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
+    // Tiles in which every (query, key) pair of this wavefront is live (all
+    // but the ones on the diagonal and the ragged last tile) skip the
+    // per-element mask.  Only the probabilities sit under the branch: the
+    // accumulators stay outside it, so no register copies arise where the
+    // two paths meet.
+    const bool full = __builtin_amdgcn_readfirstlane(
+        kw0 + 31 < Nk && (t + 1) * G::BM <= Nq && (!CAUSAL || kw0 + 31 <= t * G::BM + p.diag));
 #pragma unroll
     for (int h = 0; h < G::QB; ++h) {
       // element i: query 32h + 8(i/4) + 4g + i%4 of the tile, key my_k
       float pr[16], ds[16];
+      f32x4 lv[4], dv4[4];
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
-        const int ql = 32 * h + 8 * blk + 4 * g;
-        const f32x4 lv = *(const f32x4*)(l2 + ql);
-        const f32x4 dv4 = *(const f32x4*)(dl + ql);
+        lv[blk] = *(const f32x4*)(l2 + 32 * h + 8 * blk + 4 * g);
+        dv4[blk] = *(const f32x4*)(dl + 32 * h + 8 * blk + 4 * g);
+      }
+      if (full) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * blk + e;
-          const int q = t * G::BM + ql + e;
+        for (int i = 0; i < 16; ++i) pr[i] = fast_exp2(fmaf(s[h][i], c, -lv[i / 4][i % 4]));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int q = t * G::BM + 32 * h + 8 * (i / 4) + 4 * g + i % 4;
           const bool ok = key_ok && q < Nq && (!CAUSAL || my_k <= q + p.diag);
-          pr[i] = ok ? fast_exp2(fmaf(s[h][i], c, -lv[e])) : 0.f;
-          ds[i] = pr[i] * (dp[h][i] - dv4[e]);
+          pr[i] = ok ? fast_exp2(fmaf(s[h][i], c, -lv[i / 4][i % 4])) : 0.f;
         }
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ds[i] = pr[i] * (dp[h][i] - dv4[i / 4][i % 4]);
       const bf16x8 pp[2] = {pack8(pr), pack8(pr + 8)};
       const bf16x8 pd[2] = {pack8(ds), pack8(ds + 8)};
 #pragma unroll
