@@ -131,6 +131,8 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_kernel(BwdParams p, int nqb) {
   const float lse2 = has_keys ? lse_raw * kLog2e : 0.f;
   const float dlt = row_ok ? p.delta[grow] : 0.f;
   const float c = p.c;
+  // every query of this wavefront exists and has a finite LSE
+  const bool rows_live = __builtin_amdgcn_readfirstlane(__all(row_ok && has_keys));
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -176,6 +178,10 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_kernel(BwdParams p, int nqb) {
     const char* kb = stage_base(t);
     const char* ktb = kb + G::K_BYTES;
     const char* vb = ktb + G::KT_BYTES;
+    // Tiles in which every (query, key) pair of this wavefront is live skip
+    // the per-element mask; only the probabilities sit under the branch.
+    const bool full = __builtin_amdgcn_readfirstlane(
+        rows_live && (t + 1) * G::BN <= Nk && (!CAUSAL || (t + 1) * G::BN - 1 <= qw0 + p.diag));
 #pragma unroll
     for (int h = 0; h < G::KB; ++h) {
       f32x16 s = (f32x16){}, dp = (f32x16){};
@@ -186,15 +192,21 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_kernel(BwdParams p, int nqb) {
         const bf16x8 b = *(const bf16x8*)(vb + h * 32 * G::KS + r_off + kk * 32);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, dof[kk], dp, 0, 0, 0);
       }
-      float ds[16];
-      const int kbase = t * G::BN + 32 * h + 4 * g;
+      float pr[16], ds[16];
+      if (full) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kbase + 8 * (i >> 2) + (i & 3);
-        const bool ok = has_keys && key < Nk && (!CAUSAL || key <= my_q + p.diag);
-        const float pr = ok ? fast_exp2(fmaf(s[i], c, -lse2)) : 0.f;
-        ds[i] = pr * (dp[i] - dlt);
+        for (int i = 0; i < 16; ++i) pr[i] = fast_exp2(fmaf(s[i], c, -lse2));
+      } else {
+        const int kbase = t * G::BN + 32 * h + 4 * g;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kbase + 8 * (i >> 2) + (i & 3);
+          const bool ok = has_keys && key < Nk && (!CAUSAL || key <= my_q + p.diag);
+          pr[i] = ok ? fast_exp2(fmaf(s[i], c, -lse2)) : 0.f;
+        }
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ds[i] = pr[i] * (dp[i] - dlt);
       const bf16x8 pd[2] = {pack8(ds), pack8(ds + 8)};
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
