@@ -31,6 +31,8 @@
 // scale works.  Staging loads past the tensor ends read the last row instead
 // (unconditional loads, so none waits for another); every (query, key) pair
 // they form is masked, so its P and dS are exactly 0.
+#include <type_traits>
+
 #include "common.h"
 
 namespace eta {
@@ -349,7 +351,11 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) 
   // explicitly, so that no wait for them is left inside the tile loop.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int t = t0; t < ntiles; ++t) {
+  // One query tile.  ALL_LIVE: every (query, key) pair of the workgroup is
+  // live, so the body has no mask and no branch, and the scheduler may
+  // overlap one block's P/dS with the other block's products.
+  auto step = [&](int t, auto live_tag) __attribute__((always_inline)) {
+    constexpr bool ALL_LIVE = decltype(live_tag)::value;
     const bool more = t + 1 < ntiles;
     if (more) gload(t + 1);
     const char* qb = stage_base(t);
@@ -382,13 +388,6 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) 
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
-    // Tiles in which every (query, key) pair of this wavefront is live (all
-    // but the ones on the diagonal and the ragged last tile) skip the
-    // per-element mask.  Only the probabilities sit under the branch: the
-    // accumulators stay outside it, so no register copies arise where the
-    // two paths meet.
-    const bool full = __builtin_amdgcn_readfirstlane(
-        kw0 + 31 < Nk && (t + 1) * G::BM <= Nq && (!CAUSAL || kw0 + 31 <= t * G::BM + p.diag));
 #pragma unroll
     for (int h = 0; h < G::QB; ++h) {
       // element i: query 32h + 8(i/4) + 4g + i%4 of the tile, key my_k
@@ -399,15 +398,12 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) 
         lv[blk] = *(const f32x4*)(l2 + 32 * h + 8 * blk + 4 * g);
         dv4[blk] = *(const f32x4*)(dl + 32 * h + 8 * blk + 4 * g);
       }
-      if (full) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) pr[i] = fast_exp2(fmaf(s[h][i], c, -lv[i / 4][i % 4]));
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < 16; ++i) {
+        pr[i] = fast_exp2(fmaf(s[h][i], c, -lv[i / 4][i % 4]));
+        if constexpr (!ALL_LIVE) {
           const int q = t * G::BM + 32 * h + 8 * (i / 4) + 4 * g + i % 4;
-          const bool ok = key_ok && q < Nq && (!CAUSAL || my_k <= q + p.diag);
-          pr[i] = ok ? fast_exp2(fmaf(s[h][i], c, -lv[i / 4][i % 4])) : 0.f;
+          if (!(key_ok && q < Nq && (!CAUSAL || my_k <= q + p.diag))) pr[i] = 0.f;
         }
       }
 #pragma unroll
@@ -437,7 +433,21 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) 
     }
     if (more) lstore(t + 1);
     __syncthreads();
+  };
+  // Tiles t_lo .. t_hi-1 are all-live: every key of the block exists, the
+  // tile is whole and, under the causal mask, lies wholly below the diagonal.
+  int t_lo = ntiles, t_hi = ntiles;
+  if (k0 + G::BK <= Nk) {
+    t_hi = max(t0, Nq / G::BM);
+    t_lo = t0;
+    const int need = k0 + G::BK - 1 - p.diag;  // first query that sees every key
+    if (CAUSAL && need > 0) t_lo = max(t0, (need + G::BM - 1) / G::BM);
+    t_lo = min(t_lo, t_hi);
   }
+  int t = t0;
+  for (; t < t_lo; ++t) step(t, std::false_type{});
+  for (; t < t_hi; ++t) step(t, std::true_type{});
+  for (; t < ntiles; ++t) step(t, std::false_type{});
 
   if (!key_ok) return;
   const int64_t grow = (int64_t)bh * Nk + my_k;
