@@ -380,13 +380,13 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) 
       }
     {
       constexpr int NM = 2 * G::QB * (D / 16);
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-      for (int i = 0; i < NM - 4; ++i) {
+      for (int i = 0; i < NM - 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     }
 #pragma unroll
     for (int h = 0; h < G::QB; ++h) {
@@ -422,13 +422,13 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) 
         }
       {
         constexpr int NM = 2 * 2 * (D / 32);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-        for (int i = 0; i < NM - 4; ++i) {
+        for (int i = 0; i < NM - 8; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       }
     }
     if (more) lstore(t + 1);
