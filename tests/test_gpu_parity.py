@@ -420,6 +420,7 @@ BWD_SHAPES = [
     (1, 1, 1, 1, 128, False, 0.0884),
     (1, 2, 96, 160, 128, True, -0.2),
     (1, 2, 96, 160, 64, False, 0.0),
+    (1, 2, 384, 384, 128, True, 0.0884),  # 3 key blocks: masked diagonal tiles, then all-live ones
 ]
 
 
