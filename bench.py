@@ -6,12 +6,13 @@ One step = one pass of the hot path over one batch of synthetic input:
   * n_blocks x attn_fwd_kvblock plus the merges (block-streamed workload).
 W untimed warm-up steps, then K steps back to back on one stream, bracketed
 by HIP events recorded on that stream (torch.cuda.Event on the stream the
-kernels are launched on) and device synchronisation.  Without --warmup the
-warm-up runs for at least 0.3 s and 10 steps: an idle MI355X needs about
-0.1-0.2 s of load to leave its low clocks, and a 10-step warm-up of the
-causal B8 H16 N2048 workload (2 ms) measures ~700 instead of ~850 TFLOP/s.
-The JSON line reports the warm-up step count actually run.  Inputs are resident in
-HBM before the timed region starts.  Prints one JSON line.
+kernels are launched on) and device synchronisation.  The warm-up runs at
+least --warmup steps (default 10) and at least 0.3 s: an idle MI355X needs
+about 0.1-0.2 s of load to leave its low clocks, and a 5-step warm-up of the
+causal B8 H16 N2048 workload (1 ms) measures ~665 instead of ~840 TFLOP/s.
+The JSON line's "warmup" is the requested minimum; "warmup_steps_run" and
+"warmup_s" are what actually ran.  Inputs are
+resident in HBM before the timed region starts.  Prints one JSON line.
 
 The default workload is the causal bf16 B=8 H=16 N=2048 d=128 attention
 (TFLOP/s = 4*B*H*N^2*d/2 / time).  The CPU baseline is the fp64 oracle timed
@@ -37,7 +38,7 @@ REPO = os.path.dirname(os.path.abspath(__file__))
 if REPO not in sys.path:
     sys.path.insert(0, REPO)
 
-PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}  # dense MFMA, 256 CU x 2.4 GHz
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "fp8": 5033.2, "f32": 157.3}  # dense MFMA, 256 CU x 2.4 GHz
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 
 # rocprofv3 FETCH_SIZE/WRITE_SIZE summaries (copy-calibrated) per workload; the
@@ -78,10 +79,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed warm-up steps (default: as many as take WARMUP_SECONDS, at least 10)")
+                    help="minimum untimed warm-up steps (default 10); the warm-up also lasts at least "
+                         "WARMUP_SECONDS")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--no-measured-peak", action="store_true",
+                    help="skip the matrix-core peak loop that follows the timed region")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain copy kernel of known size (HBM counter calibration)")
     return ap.parse_args()
@@ -91,24 +95,109 @@ WARMUP_SECONDS = 0.3
 
 
 def warm_up(step, warmup):
-    """Run the untimed warm-up; returns the number of steps run.  `warmup`
-    steps when given; otherwise at least 10 steps and WARMUP_SECONDS of them
-    (the host waits for the GPU every 8 steps, so the time is the GPU's)."""
+    """Run the untimed warm-up: at least `warmup` steps (10 when None) and at
+    least WARMUP_SECONDS of them (the host waits for the GPU every 8 steps, so
+    the time is the GPU's).  Returns (steps run, seconds)."""
     import torch
 
-    if warmup is not None:
-        for _ in range(warmup):
-            step()
-        torch.cuda.synchronize()
-        return warmup
+    min_steps = 10 if warmup is None else max(0, warmup)
     n, t0 = 0, time.perf_counter()
-    while n < 10 or time.perf_counter() - t0 < WARMUP_SECONDS:
+    while n < min_steps or time.perf_counter() - t0 < WARMUP_SECONDS:
         step()
         n += 1
         if n % 8 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-    return n
+    return n, time.perf_counter() - t0
+
+
+MFMA_KINDS = {"bf16": 0, "f16": 1, "fp8": 2, "f32": 3}
+
+
+def mfma_peak_run(eta, kind, iters, stream, repeats=5):
+    """Median TFLOP/s of `repeats` launches of the matrix-core loop (one 8-wavefront
+    workgroup per compute unit), each timed with events on `stream`."""
+    import torch
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty((cus * eta.MFMA_PEAK_THREADS,), device="cuda")
+    flop = eta.mfma_peak_flop(kind, cus, iters)
+    eta.mfma_peak(kind, cus, iters, out, stream)  # untimed first launch
+    times = []
+    for _ in range(repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        eta.mfma_peak(kind, cus, iters, out, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = sorted(times)[len(times) // 2]
+    return flop / (ms * 1e-3) / 1e12, ms, cus, flop
+
+
+def measured_peak(eta, dtype, stream):
+    """Measured dense matrix-core peak for the workload's dtype, run right after the timed
+    region (the clocks are still at their working level).  The fp8 path's Q.K runs at the fp8
+    rate; its figure is reported against the fp8 loop."""
+    kind = {"bf16": "bf16", "fp8": "fp8", "f32": "f32"}[dtype]
+    iters = {"bf16": 20000, "fp8": 10000, "f32": 5000}[kind]
+    tf, ms, cus, _ = mfma_peak_run(eta, MFMA_KINDS[kind], iters, stream)
+    return {"kind": kind, "value": round(tf, 1), "unit": "TFLOP/s", "ms_per_launch": round(ms, 4),
+            "workgroups": cus, "iters": iters,
+            "loop": "attn_mfma_peak: 8 wavefronts per compute unit, 4 independent MFMA chains each"}
+
+
+def bench_mfma(args, name, cfg):
+    """The matrix-core throughput loop alone: TFLOP/s against the datasheet's dense peak."""
+    import torch
+
+    import exact_tiled_attention_15_amd as eta
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    kind = cfg["mfma"]
+    iters = cfg["iters"]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty((cus * eta.MFMA_PEAK_THREADS,), device="cuda")
+    step = lambda: eta.mfma_peak(MFMA_KINDS[kind], cus, iters, out, stream)
+    warmup, warmup_s = warm_up(step, args.warmup)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+    flop = eta.mfma_peak_flop(MFMA_KINDS[kind], cus, iters)
+    tf = flop / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[kind]
+    out_line = {
+        "metric": f"dense {kind} MFMA throughput loop TFLOP/s and % of MI355X datasheet peak",
+        "value": round(tf, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": 10 if args.warmup is None else args.warmup,
+        "warmup_steps_run": warmup,
+        "warmup_s": round(warmup_s, 3),
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": kind,
+        "data": "register operands, no memory traffic",
+        "config": {"workload": name, "workgroups": cus, "threads": eta.MFMA_PEAK_THREADS, "iters": iters,
+                   "chains_per_wavefront": 4},
+        "pct_of_peak": round(100 * tf / peak, 2),
+        "wall_s_timed": round(t_wall, 4),
+        "roofline": {"bound": "mfma", "kernel": f"mfma_peak_kernel<{MFMA_KINDS[kind]}>", "achieved": round(tf, 1),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(tf / peak, 4), "traffic": None,
+                     "launches_per_step": 1},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out_line), flush=True)
 
 
 def cpu_model():
@@ -138,6 +227,8 @@ def main():
     cfg = configs.WORKLOADS[name]
     if cfg.get("kind") == "w4a16":
         return bench_w4a16(args, name, cfg)
+    if cfg.get("kind") == "mfma":
+        return bench_mfma(args, name, cfg)
     seed = configs.seed_of(name)
     B, H, Nq, Nk, d = cfg["B"], cfg["H"], cfg["Nq"], cfg["Nk"], cfg["d"]
     causal = cfg["causal"]
@@ -233,7 +324,8 @@ def main():
         t = {n: dv(x[n]) for n in ("q8", "k8", "v8", "q_scale", "k_scale", "v_scale")}
         o = torch.empty((B, H, Nq, d), device="cuda")
         lse = torch.empty((B, H, Nq), device="cuda")
-        fp8_fn = eta.attn_fwd_fp8_pv8 if cfg.get("pv8") else eta.attn_fwd_fp8
+        fp8_fn = (eta.attn_fwd_fp8_pv8 if cfg.get("pv8") else
+                  eta.attn_fwd_fp8_qk16 if cfg.get("qk16") else eta.attn_fwd_fp8)
         step = lambda: fp8_fn(t["q8"], t["k8"], t["v8"], t["q_scale"], t["k_scale"], t["v_scale"],
                               o, lse, causal, scale, stream)
         kernel = "fwd_fp8_kernel"
@@ -242,7 +334,7 @@ def main():
     if not cfg.get("host_kv"):
         transfer = None
     flop = configs.workload_flops(name)
-    warmup = warm_up(step, args.warmup)
+    warmup, warmup_s = warm_up(step, args.warmup)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
     e0.record(stream)
@@ -262,6 +354,9 @@ def main():
         torch.neg(src, out=dst)
         torch.cuda.synchronize()
 
+    mpeak = None if args.no_measured_peak else measured_peak(eta, dtype, stream)
+    if mpeak is not None:
+        mpeak["frac"] = round(tflops / mpeak["value"], 4)
     roofline = {
         "bound": "mfma",
         "kernel": kernel,
@@ -286,7 +381,9 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": warmup,
+        "warmup": 10 if args.warmup is None else args.warmup,
+        "warmup_steps_run": warmup,
+        "warmup_s": round(warmup_s, 3),
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -296,8 +393,10 @@ def main():
         "config": {"workload": name, "B": B, "H": H, "Nq": Nq, "Nk": Nk, "d": d, "causal": causal,
                    "scale": scale, "seed": seed},
         "pct_of_peak": round(100 * tflops / peak, 2),
+        "pct_of_measured_peak": None if mpeak is None else round(100 * mpeak["frac"], 2),
         "wall_s_timed": round(t_wall, 4),
         "roofline": roofline,
+        "measured_peak": mpeak,
         "cpu_baseline": cpu,
     }
     if transfer is not None:
@@ -391,7 +490,7 @@ def host_kv_parts(args, eta, q, kh, vh, pos, o, lse, work, causal, scale, stream
         eta.attn_fwd_ring(q, kd, vd, pos, o, lse, work, causal, 0, scale, stream)
 
     def timed(fn, n):
-        warm_up(fn, None if args.warmup is None else max(1, args.warmup // 2))
+        warm_up(fn, args.warmup)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(n):
@@ -437,7 +536,7 @@ def bench_w4a16(args, name, cfg):
         state["i"] += 1
         eta.w4a16_gemm(x, p, sc, z, y, work, G, stream)
 
-    warmup = warm_up(step, args.warmup)
+    warmup, warmup_s = warm_up(step, args.warmup)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
     e0.record(stream)
@@ -475,7 +574,9 @@ def bench_w4a16(args, name, cfg):
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": warmup,
+        "warmup": 10 if args.warmup is None else args.warmup,
+        "warmup_steps_run": warmup,
+        "warmup_s": round(warmup_s, 3),
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",

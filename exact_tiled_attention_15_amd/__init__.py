@@ -12,6 +12,11 @@ from ._lib import (  # noqa: F401
     ATTN_ERR_UNSUPPORTED,
     ATTN_OK,
     FP8_TILE,
+    MFMA_BF16,
+    MFMA_F16,
+    MFMA_F32,
+    MFMA_FP8,
+    MFMA_PEAK_THREADS,
     W4A16_GROUP,
     W4A16_MAX_M,
     W4A16_TOKENS_PER_PASS,
@@ -29,6 +34,9 @@ from ._lib import (  # noqa: F401
     attn_merge,
     bwd_work_floats,
     lib,
+    mfma_dot,
+    mfma_peak,
+    mfma_peak_flop,
     ring_stage_bytes,
     ring_work_floats,
     status_str,

@@ -1,4 +1,4 @@
-"""ctypes binding of libattn.so (include/attn.h, include/w4a16.h).
+"""ctypes binding of libattn.so (include/attn.h, include/w4a16.h, include/mfma_probe.h).
 
 Argument marshalling only: every function here checks that the torch tensors
 it is handed have the dtype/shape/device the C entry point documents, passes
@@ -21,6 +21,8 @@ FP8_TILE = 128
 W4A16_GROUP = 128
 W4A16_MAX_M = 4096
 W4A16_TOKENS_PER_PASS = 16
+MFMA_BF16, MFMA_F16, MFMA_FP8, MFMA_F32 = 0, 1, 2, 3
+MFMA_PEAK_THREADS = 512
 
 
 class AttnError(RuntimeError):
@@ -75,6 +77,12 @@ def lib() -> ctypes.CDLL:
     L.w4a16_work_floats.argtypes = [i64, i64, i64, i64]
     L.w4a16_gemm.restype = i
     L.w4a16_gemm.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp]
+    L.attn_mfma_peak_flop.restype = ctypes.c_double
+    L.attn_mfma_peak_flop.argtypes = [i, i, i]
+    L.attn_mfma_peak.restype = i
+    L.attn_mfma_peak.argtypes = [i, i, i, vp, vp]
+    L.attn_mfma_dot.restype = i
+    L.attn_mfma_dot.argtypes = [i, vp, vp, vp, vp]
     _lib = L
     return L
 
@@ -323,3 +331,26 @@ def w4a16_gemm(x, packed, scales, zeros, y, work=None, group: int = W4A16_GROUP,
         _want(work, torch.float32, (nw,), "work")
     _check(lib().w4a16_gemm(_ptr(x), _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(y),
                             _ptr(work) if nw else None, M, N, K, group, _stream(stream)), "w4a16_gemm")
+
+
+def mfma_peak_flop(kind: int, workgroups: int, iters: int) -> float:
+    """FLOP of one attn_mfma_peak launch."""
+    return lib().attn_mfma_peak_flop(kind, workgroups, iters)
+
+
+def mfma_peak(kind: int, workgroups: int, iters: int, out, stream=None):
+    """Matrix-core throughput loop; out: fp32 device tensor of workgroups * MFMA_PEAK_THREADS."""
+    _want(out, torch.float32, (workgroups * MFMA_PEAK_THREADS,), "out")
+    _check(lib().attn_mfma_peak(kind, workgroups, iters, _ptr(out), _stream(stream)), "attn_mfma_peak")
+
+
+def mfma_dot(kind: int, a, b, c, stream=None):
+    """C[32,32] = A[32,64] B (b holds B's columns as rows) on one matrix-core tile: a, b uint8
+    e4m3 codes (MFMA_FP8) or bfloat16 / float16 (MFMA_BF16 / MFMA_F16); c float32."""
+    dt = {MFMA_FP8: torch.uint8, MFMA_BF16: torch.bfloat16, MFMA_F16: torch.float16}.get(kind)
+    if dt is None:
+        raise ValueError(f"unknown kind {kind}")
+    _want(a, dt, (32, 64), "a")
+    _want(b, dt, (32, 64), "b")
+    _want(c, torch.float32, (32, 32), "c")
+    _check(lib().attn_mfma_dot(kind, _ptr(a), _ptr(b), _ptr(c), _stream(stream)), "attn_mfma_dot")

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(REPO_DIR, "include")
 BUILD_DIR = os.path.join(REPO_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libattn.so")
-SOURCES = ["fwd_bf16.hip", "fwd_fp8.hip", "fwd_f32.hip", "merge.hip", "bwd_bf16.hip", "w4a16.hip", "api.cpp"]
+SOURCES = ["fwd_bf16.hip", "fwd_fp8.hip", "fwd_f32.hip", "merge.hip", "bwd_bf16.hip", "w4a16.hip", "mfma_probe.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -27,7 +27,7 @@ WORKLOADS = {
     # then its predecessors' (hop order 7, 6, .., 0).
     "bf16_causal_ring_B1_H16_N65536_R8_d128": dict(index=5, B=1, H=16, Nq=8192, Nk=65536, d=128,
                                                    dtype="bf16", causal=True, n_blocks=8,
-                                                   q_pos0=57344, ring=True, oracle_rows=256),
+                                                   q_pos0=57344, ring=True, oracle_rows=512),
     # The kvblocks share with the 8 K/V blocks arriving from page-locked host memory,
     # each block's transfer overlapped with the previous block's attention (the host link
     # stands in for the ring's peer link).
@@ -43,6 +43,12 @@ WORKLOADS = {
     "fp8_B4_H16_N4096_d128": dict(index=4, B=4, H=16, Nq=4096, Nk=4096, d=128, dtype="fp8",
                                   causal=False, outlier_frac=0.01, outlier_mult=20.0,
                                   oracle_rows=512, rotate=True),
+    # The same workload (same seed and draws) without the rotation, Q.K on fp16 matrix cores
+    # over the widened codes (attn_fwd_fp8_qk16): the form that meets the fp8 bar on an
+    # un-rotated outlier channel.
+    "fp8_norot_qk16_B4_H16_N4096_d128": dict(index=4, B=4, H=16, Nq=4096, Nk=4096, d=128, dtype="fp8",
+                                             causal=False, outlier_frac=0.01, outlier_mult=20.0,
+                                             oracle_rows=512, rotate=False, qk16=True),
     # The same recipe with the probabilities in e4m3 too (both products on fp8 matrix cores).
     "fp8_pv8_B4_H16_N4096_d128": dict(index=7, B=4, H=16, Nq=4096, Nk=4096, d=128, dtype="fp8",
                                       causal=False, outlier_frac=0.01, outlier_mult=20.0,
@@ -58,6 +64,13 @@ WORKLOADS = {
                                                group=128, seed=1008, weight_copies=4),
     "w4a16_decode_M16_N8192_K28672_G128": dict(index=9, kind="w4a16", M=16, N=8192, K=28672,
                                                group=128, seed=1009, weight_copies=4),
+    # Matrix-core throughput loops (attn_mfma_peak): one workgroup of 8 wavefronts per compute
+    # unit, four independent accumulator chains per wavefront, register operands.  The measured
+    # peak that the attention workloads are also reported against.
+    "mfma_peak_bf16": dict(index=11, kind="mfma", mfma="bf16", iters=100000),
+    "mfma_peak_fp8": dict(index=12, kind="mfma", mfma="fp8", iters=50000),
+    "mfma_peak_f16": dict(index=13, kind="mfma", mfma="f16", iters=100000),
+    "mfma_peak_f32": dict(index=14, kind="mfma", mfma="f32", iters=50000),
 }
 
 HEADLINE = "bf16_causal_B8_H16_N2048_d128"

@@ -4,6 +4,7 @@
 // The one HIP object the library creates itself is attn_fwd_ring_host's copy
 // stream (with its events), once per device.
 #include "attn.h"
+#include "mfma_probe.h"
 #include "w4a16.h"
 
 #include <algorithm>
@@ -511,6 +512,26 @@ attn_status w4a16_gemm(const void* x, const uint32_t* packed, const void* scales
     if (attn_status s = from_hip(eta::launch_w4a16(p, pl, cu > 0 ? cu : 256, (hipStream_t)stream))) return s;
   }
   return ATTN_OK;
+}
+
+double attn_mfma_peak_flop(int kind, int workgroups, int iters) {
+  if (workgroups < 1 || workgroups > (1 << 20) || iters < 1 || iters > (1 << 24)) return 0.0;
+  const double per = eta::mfma_flop_per_instruction(kind);
+  return per * 4.0 * double(iters) * 8.0 * double(workgroups);
+}
+
+attn_status attn_mfma_peak(int kind, int workgroups, int iters, float* out, void* stream) {
+  if (workgroups < 1 || workgroups > (1 << 20) || iters < 1 || iters > (1 << 24)) return ATTN_ERR_INVALID;
+  if (attn_status s = check_ptrs4({out}, false)) return s;
+  if (kind < ATTN_MFMA_BF16 || kind > ATTN_MFMA_F32) return ATTN_ERR_UNSUPPORTED;
+  return from_hip(eta::launch_mfma_peak(kind, workgroups, iters, out, (hipStream_t)stream));
+}
+
+attn_status attn_mfma_dot(int kind, const void* a, const void* b, float* c, void* stream) {
+  if (attn_status s = check_ptrs16({a, b})) return s;
+  if (attn_status s = check_ptrs4({c}, false)) return s;
+  if (kind < ATTN_MFMA_BF16 || kind > ATTN_MFMA_FP8) return ATTN_ERR_UNSUPPORTED;
+  return from_hip(eta::launch_mfma_dot(kind, a, b, c, (hipStream_t)stream));
 }
 
 }  // extern "C"

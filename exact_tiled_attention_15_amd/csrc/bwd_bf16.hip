@@ -365,7 +365,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) 
     const float* l2 = (const float*)(dotb + G::T_BYTES);
     const float* dl = l2 + G::BM;
     // S and dP of both 32-query blocks: 4 (D/16) MFMA chains, LDS reads run
-    // four fragments ahead.
+    // eight fragments ahead (nothing else on the SIMD covers their latency).
     f32x16 s[G::QB], dp[G::QB];
 #pragma unroll
     for (int h = 0; h < G::QB; ++h) s[h] = dp[h] = (f32x16){};

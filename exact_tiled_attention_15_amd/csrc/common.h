@@ -113,6 +113,12 @@ struct BwdParams {
 };
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t s);
 
+// Matrix-core measurements (mfma_probe.hip): kind 0 bf16, 1 fp16, 2 fp8
+// (f8f6f4 with unit scales), 3 fp32.
+double mfma_flop_per_instruction(int kind);
+hipError_t launch_mfma_peak(int kind, int workgroups, int iters, float* out, hipStream_t s);
+hipError_t launch_mfma_dot(int kind, const void* a, const void* b, float* c, hipStream_t s);
+
 // ------------------------------------------------------------ device helpers
 // Workgroup -> (query block, b*h slice).  Workgroups are dealt to the 8 XCDs
 // round-robin (XCD = blockIdx % 8); when the slices divide evenly, each XCD is

@@ -16,10 +16,15 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
- *    allocates nothing, keeps no global state, and never synchronises the host:
- *    each call validates its arguments on the host, enqueues its kernels on
- *    `stream` (a hipStream_t; NULL means the default stream) and returns.
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller (except the
+ *    host-resident K/V blocks of attn_fwd_ring_host).  The library allocates no
+ *    memory and never synchronises the host: each call validates its arguments
+ *    on the host, enqueues its kernels on `stream` (a hipStream_t; NULL means
+ *    the default stream) and returns.  Global state is limited to two caches
+ *    that live until the process ends and never change a result: each device's
+ *    compute-unit count (read once, used to size the W4A16 grid), and
+ *    attn_fwd_ring_host's per-device copy stream with five events, created on
+ *    that entry point's first call on the device and guarded by a mutex.
  *  - Layout: contiguous [B, H, N, d] row-major, d innermost; per-row outputs
  *    (lse, m, l) are contiguous [B, H, N].  Q/K/V/O pointers must be 16-byte
  *    aligned; per-row pointers 4-byte aligned.  Outputs must not alias inputs.
@@ -73,12 +78,13 @@ const char* attn_status_str(attn_status s);
  *   o   bf16 [B,H,Nq,d]     O = P V with P = softmax of the allowed scores,
  *                           accumulated in fp32, rounded to nearest-even once.
  *   lse fp32 [B,H,Nq]       may be NULL (not written).
- * The outer loop runs over 128-row query blocks (one workgroup each, spread
- * over all compute units: sequence-length parallelism); the inner loop streams
- * 64-key K/V tiles through LDS, keeps the running max / normaliser per row and
- * divides by the normaliser once after the loop ("FlashAttention-2", Systems
- * analysis wiki, "Technical architecture and working principles", items 1-3).
- * Causal key tiles above the diagonal are skipped wholesale.
+ * The outer loop runs over 256-row query blocks (one workgroup of 8
+ * wavefronts each, spread over all compute units: sequence-length
+ * parallelism); the inner loop streams 128-key K/V tiles through LDS (double
+ * buffered), keeps the running max / normaliser per row and divides by the
+ * normaliser once after the loop ("FlashAttention-2", Systems analysis wiki,
+ * "Technical architecture and working principles", items 1-3).  Causal key
+ * tiles above the diagonal are skipped wholesale.
  */
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int H, int Nq, int Nk, int d, int causal, float scale,

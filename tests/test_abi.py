@@ -10,7 +10,8 @@ import pytest
 import exact_tiled_attention_15_amd as eta
 
 REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(REPO, "include", h) for h in ("attn.h", "w4a16.h")]
+HEADERS = [os.path.join(REPO, "include", h) for h in sorted(os.listdir(os.path.join(REPO, "include")))
+           if h.endswith(".h")]
 
 P16 = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation
 P16b = ctypes.c_void_p(0x20000)
@@ -32,7 +33,8 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     names = declared_functions()
     assert {"attn_fwd", "attn_fwd_f32", "attn_fwd_kvblock", "attn_merge", "attn_fwd_fp8",
-            "attn_abi_version", "attn_status_str", "w4a16_gemm", "w4a16_work_floats"} <= set(names)
+            "attn_abi_version", "attn_status_str", "w4a16_gemm", "w4a16_work_floats",
+            "attn_mfma_peak", "attn_mfma_dot", "attn_mfma_peak_flop"} <= set(names)
     L = eta.lib()
     for n in names:
         assert hasattr(L, n), f"{n} not exported by libattn.so"
@@ -211,3 +213,20 @@ def w4(*, x=P16, packed=P16b, scales=P4, zeros=P4, y=P4, work=NUL, M=4, N=32, K=
 ])
 def test_w4a16_rejects_bad_arguments(kw, want):
     assert w4(**kw) == want
+
+
+def test_mfma_probe_validation_and_flop():
+    L = eta.lib()
+    assert L.attn_mfma_peak(eta.MFMA_BF16, 0, 10, P4, None) == eta.ATTN_ERR_INVALID
+    assert L.attn_mfma_peak(eta.MFMA_BF16, 4, 0, P4, None) == eta.ATTN_ERR_INVALID
+    assert L.attn_mfma_peak(eta.MFMA_BF16, 4, 10, NUL, None) == eta.ATTN_ERR_INVALID
+    assert L.attn_mfma_peak(eta.MFMA_BF16, 4, 10, ctypes.c_void_p(0x50002), None) == eta.ATTN_ERR_INVALID
+    assert L.attn_mfma_peak(7, 4, 10, P4, None) == eta.ATTN_ERR_UNSUPPORTED
+    assert L.attn_mfma_dot(eta.MFMA_FP8, NUL, P16b, P4, None) == eta.ATTN_ERR_INVALID
+    assert L.attn_mfma_dot(eta.MFMA_FP8, MIS, P16b, P4, None) == eta.ATTN_ERR_INVALID
+    assert L.attn_mfma_dot(eta.MFMA_F32, P16, P16b, P4, None) == eta.ATTN_ERR_UNSUPPORTED
+    # FLOP per launch: workgroups x 8 wavefronts x iters x 4 instructions x FLOP per instruction
+    assert eta.mfma_peak_flop(eta.MFMA_BF16, 256, 100) == 256 * 8 * 100 * 4 * 2 * 32 * 32 * 16
+    assert eta.mfma_peak_flop(eta.MFMA_FP8, 3, 5) == 3 * 8 * 5 * 4 * 2 * 32 * 32 * 64
+    assert eta.mfma_peak_flop(eta.MFMA_F32, 1, 1) == 8 * 4 * 2 * 32 * 32 * 2
+    assert eta.mfma_peak_flop(9, 1, 1) == 0 and eta.mfma_peak_flop(eta.MFMA_BF16, 0, 1) == 0

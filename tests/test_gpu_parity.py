@@ -122,7 +122,7 @@ def test_scale_sign_and_zero(scale):
     o, lse = _run_fwd(qb, kb, vb, True, scale)
     ro, rl = oracle.attention(oracle.decode_bf16(qb), oracle.decode_bf16(kb), oracle.decode_bf16(vb), True, scale)
     compare_o(o, ro, BF16_BAR, "O")
-    compare_lse(lse, rl, "LSE", bar=1e-3 * max(1.0, abs(scale) * 10))
+    compare_lse(lse, rl, "LSE")
 
 
 def test_empty_causal_rows():
@@ -215,12 +215,28 @@ FP8_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("mode", ["qk16", "fp8"])
-@pytest.mark.parametrize("Nq,Nk,d,causal,rotate,outliers", FP8_SHAPES)
+# The fp8 matrix cores sum one instruction's products with limited alignment precision
+# (tests/test_gpu_mfma_fp8.py measures it): an un-rotated x20 channel shared by Q and K makes one
+# product per score ~400 times the others, and the scores move by ~0.1 in log2 units.  attn_fwd_fp8
+# (Q.K on fp8 MFMA) therefore misses the fp8 bar on such inputs; the rotation of the same passage
+# (incoherent processing) is what brings it inside.  These cases are expected failures, strictly:
+# an unexpected pass fails the run.  attn_fwd_fp8_qk16 (Q.K on fp16 MFMA) meets the bar on them.
+XFAIL_FP8_UNROTATED = pytest.mark.xfail(
+    strict=True, raises=AssertionError,
+    reason="fp8 MFMA alignment precision on an un-rotated outlier channel: Q.K error ~0.1 in log2 units")
+
+
+def _fp8_cases():
+    for shape in FP8_SHAPES:
+        for mode in ("qk16", "fp8"):
+            _, _, _, _, rotate, outliers = shape
+            marks = [XFAIL_FP8_UNROTATED] if (mode == "fp8" and outliers and not rotate) else []
+            yield pytest.param(*shape, mode, marks=marks)
+
+
+@pytest.mark.parametrize("Nq,Nk,d,causal,rotate,outliers,mode", list(_fp8_cases()))
 def test_fp8_small_shapes(Nq, Nk, d, causal, rotate, outliers, mode):
     say(f"fp8 mode={mode} Nq={Nq} Nk={Nk} d={d} causal={causal} rotate={rotate} outliers={outliers}")
-    if mode == "fp8" and outliers and not rotate:
-        pytest.skip("fp8 MFMA Q.K with an un-rotated outlier channel: covered by test_fp8_mfma_outliers_need_rotation")
     x = _fp8_problem(1, 2, Nq, Nk, d, 1000 + Nq + Nk, outliers=outliers, rotate=rotate)
     scale = 1.0 / math.sqrt(d)
     o, lse = _run_fp8(x, causal, scale, mode)
@@ -285,14 +301,16 @@ def test_workload_f32_B1_H2_N256_d64():
     compare_lse(host(lse), rl, "LSE")
 
 
-@pytest.mark.parametrize("name,rows_per_head", [("bf16_causal_B8_H16_N2048_d128", 256),
+@pytest.mark.parametrize("name,rows_per_head", [("bf16_causal_B8_H16_N2048_d128", "all"),
                                                 ("bf16_causal_B1_H8_N32768_d128", 512)])
 def test_workload_bf16_causal(name, rows_per_head):
-    say(name)
+    """Full-size causal workloads: every row of every head of the headline shape, and the
+    workload's 512 sampled rows per head (plus the first four and the last) of the long one."""
+    say(f"{name} rows/head={rows_per_head}")
     cfg, seed = configs.WORKLOADS[name], configs.seed_of(name)
     x = inputs.make_inputs(cfg, seed)
     o, lse = _run_fwd(x["q"], x["k"], x["v"], True, configs.scale_of(name))
-    rows = _sample_rows(cfg["Nq"], rows_per_head, seed)
+    rows = np.arange(cfg["Nq"]) if rows_per_head == "all" else _sample_rows(cfg["Nq"], rows_per_head, seed)
     ro, rl = oracle.attention(oracle.decode_bf16(x["q"]), oracle.decode_bf16(x["k"]), oracle.decode_bf16(x["v"]),
                               True, configs.scale_of(name), rows=rows)
     compare_o(o[:, :, rows], ro, BF16_BAR, f"O ({len(rows)} rows/head)")
@@ -328,7 +346,8 @@ def test_workload_kv_blocks():
     # block-streamed result equals one-pass attention over all 65536 keys
     compare_o(o_b, o_1, BF16_BAR, "blocks vs one-pass (all rows)")
     compare_lse(l_b, l_1, "blocks vs one-pass LSE")
-    rows = _sample_rows(Nq, 256, seed)
+    rows = _sample_rows(Nq, cfg["oracle_rows"], seed)
+    say(f"  oracle on {len(rows)} rows/head")
     ro, rl = oracle.attention(oracle.decode_bf16(x["q"]), oracle.decode_bf16(x["k"]), oracle.decode_bf16(x["v"]),
                               False, scale, rows=rows)
     compare_o(o_b[:, :, rows], ro, BF16_BAR, "blocks vs oracle")
@@ -533,23 +552,18 @@ def test_workload_ring_share():
     compare_lse(l_r[:, :, rows], rl, "ring LSE vs oracle")
 
 
-@pytest.mark.parametrize("rotate,mode", [(False, "qk16"), (True, "fp8"), (True, "qk16"), (False, "fp8")])
+@pytest.mark.parametrize("rotate,mode", [(False, "qk16"), (True, "fp8"), (True, "qk16"),
+                                         pytest.param(False, "fp8", marks=XFAIL_FP8_UNROTATED)])
 def test_workload_fp8(rotate, mode):
+    """The fp8 workload at full size, every row of every head, both input variants (un-rotated and
+    Hadamard-rotated) on both Q.K forms; the fp8-MFMA form on un-rotated inputs is an expected
+    failure (see XFAIL_FP8_UNROTATED)."""
     name = "fp8_B4_H16_N4096_d128"
-    say(f"{name} rotate={rotate} mode={mode}")
+    say(f"{name} rotate={rotate} mode={mode} rows/head=all")
     cfg, seed = configs.WORKLOADS[name], configs.seed_of(name)
     x = inputs.make_inputs(cfg, seed, rotate=rotate)
     scale = configs.scale_of(name)
     o, lse = _run_fp8(x, False, scale, mode)
-    rows = _sample_rows(cfg["Nq"], 128, seed)
-    ro, rl = _fp8_ref(x, False, scale, rows=rows)
-    got = o[:, :, rows]
-    if mode == "fp8" and not rotate:
-        # fp8 matrix cores on an un-rotated outlier channel: reported, relative error gated
-        err = float(np.abs(got - ro).max())
-        rel = float(np.linalg.norm(got - ro) / np.linalg.norm(ro))
-        say(f"  un-rotated fp8 MFMA (reported): max_abs={err:.3e} rel_frob={rel:.3e}")
-        assert rel <= FP8_BAR[1]
-        return
-    compare_o(got, ro, FP8_BAR, f"O fp8 ({len(rows)} rows/head)")
-    compare_lse(lse[:, :, rows], rl, "LSE fp8")
+    ro, rl = _fp8_ref(x, False, scale)
+    compare_o(o, ro, FP8_BAR, f"O fp8 ({cfg['Nq']} rows/head)")
+    compare_lse(lse, rl, "LSE fp8")
