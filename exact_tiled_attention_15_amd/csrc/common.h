@@ -165,6 +165,34 @@ __device__ inline void load_lds16(const void* src, unsigned lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(src) : "memory", "m0");
 }
 
+// Wave-wide global->LDS transfers through a buffer resource: 16 bytes per lane
+// from rsrc.base + soff + voff into LDS at lds + 16 * lane; soff and lds then
+// advance by SSTEP and LSTEP bytes inside the same statement, so a run of
+// transfers needs no precomputed addresses.  As with load_lds16, the kernel
+// orders the transfers itself (vmcnt(0) and a barrier before the data is read).
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+template <int SSTEP, int LSTEP>
+__device__ inline void buf_lds16(i32x4 rsrc, unsigned voff, unsigned& soff, unsigned& lds) {
+  asm volatile(
+      "s_mov_b32 m0, %[l]\n\tbuffer_load_dwordx4 %[v], %[r], %[s] offen lds\n\t"
+      "s_add_u32 %[s], %[s], %[ss]\n\ts_add_u32 %[l], %[l], %[ls]"
+      : [s] "+s"(soff), [l] "+s"(lds)
+      : [v] "v"(voff), [r] "s"(rsrc), [ss] "i"(SSTEP), [ls] "i"(LSTEP)
+      : "memory", "m0", "scc");
+}
+// Raw buffer resource starting at base (no range check is relied on: every
+// offset the kernels use stays inside the tensor).
+__device__ inline i32x4 buffer_rsrc(const void* base) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  i32x4 r = {(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), -1, 0x00020000};
+  r[0] = __builtin_amdgcn_readfirstlane(r[0]);
+  r[1] = __builtin_amdgcn_readfirstlane(r[1]);
+  return r;
+}
+__device__ inline unsigned lds_offset(const void* x) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)x;
+}
+
 // ---------------------------------------------------------------- V^T tile
 // The P.V product reads V with keys along the MFMA k dimension, i.e. 8 keys of
 // one column d per lane.  V is therefore staged into LDS transposed: one LDS row

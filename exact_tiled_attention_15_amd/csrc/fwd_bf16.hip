@@ -280,21 +280,62 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
     load_k(0);
     gload_v(0);
   }
+  // Q block: contiguous 1 KiB transfers straight into the second K/V stage
+  // (rows 0..127 into the K stage, 128..255 into the V stage), each row's
+  // 16-byte chunks permuted (chunk c of block row r at slot c ^ (r mod d/8))
+  // so the fragment reads below, 32 rows at one column, hit distinct banks.
+  // Transfer j covers rows QR*j .. +QR-1; wavefront w issues j = w + 8n, so
+  // j mod 4 = w mod 4 and each lane's source offset is one constant.
+  constexpr int QR = 1024 / (2 * D);              // rows per transfer
+  constexpr int QT = G::BM / QR;                  // transfers per Q block
+  constexpr int QPW = QT / W;                     // per wavefront
+  constexpr int CPQ = D / 8;                      // 16-byte chunks per row
+  char* const q_lo = smem + G::K_BYTES;                     // rows 0 .. BM/2-1
+  char* const q_hi = smem + 2 * G::K_BYTES + G::V_BYTES;    // rows BM/2 ..
   {
-    const bool ok = my_q < Nq;
-    const u32x4* src = (const u32x4*)(qg + (int64_t)min(my_q, Nq - 1) * D + g * 8);
-    u32x4 raw[D / 16];
+    const int rin = lane / CPQ, jc = lane % CPQ;
+    const int swz = (QR * (wave & 3) + rin) & (CPQ - 1);
+    const unsigned q_lane = (unsigned)(rin * D + 8 * (jc ^ swz)) * 2u;
+    const i32x4 rsrc = buffer_rsrc(qg + (int64_t)q0 * D);
+    if (q0 + G::BM <= Nq) {
+      unsigned soff = __builtin_amdgcn_readfirstlane(1024u * wave);
+      unsigned lds = __builtin_amdgcn_readfirstlane(lds_offset(q_lo) + 1024u * wave);
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) raw[kk] = src[kk * 2];
+      for (int n = 0; n < QPW / 2; ++n) buf_lds16<8192, 8192>(rsrc, q_lane, soff, lds);
+      lds = __builtin_amdgcn_readfirstlane(lds_offset(q_hi) + 1024u * wave);
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      u32x4 x = (raw[kk] & p.q_and) ^ p.q_xor;
-      if (!ok) x = (u32x4){0u, 0u, 0u, 0u};
-      qf[kk] = __builtin_bit_cast(bf16x8, x);
+      for (int n = 0; n < QPW / 2; ++n) buf_lds16<8192, 8192>(rsrc, q_lane, soff, lds);
+    } else {  // last block of a slice: rows past Nq read the last row
+      unsigned soff = 0;
+#pragma unroll 1
+      for (int n = 0; n < QPW; ++n) {
+        const int j = wave + W * n;
+        unsigned lds = __builtin_amdgcn_readfirstlane(lds_offset(n < QPW / 2 ? q_lo : q_hi) +
+                                                      1024u * (j % (QT / 2)));
+        const int row = min(q0 + QR * j + rin, Nq - 1) - q0;
+        buf_lds16<0, 0>(rsrc, (unsigned)(row * D * 2) + (q_lane - (unsigned)(rin * D * 2)), soff, lds);
+      }
     }
   }
   if (ntiles > 0) lstore_v(0);
   publish();
+  // Q fragment (B operand of S^T = K Q^T): row my_q, d = kk*16 + g*8 .. +8,
+  // i.e. chunk 2kk + g of block row r = 32 wave + r32, at slot (2kk + g) ^ (r32
+  // mod d/8).  Rows past Nq are zeroed.
+  {
+    const bool ok = my_q < Nq;
+    const char* qrow = (wave < W / 2 ? q_lo : q_hi) + (r32 + 32 * (wave % (W / 2))) * (2 * D);
+    const int x = g ^ (r32 & (CPQ - 1));
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      u32x4 v = *(const u32x4*)(qrow + 16 * ((2 * kk) ^ x));
+      v = (v & p.q_and) ^ p.q_xor;
+      if (!ok) v = (u32x4){0u, 0u, 0u, 0u};
+      qf[kk] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  // the second stage is refilled by the first tile's transfers
+  __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const bool more = t + 1 < ntiles;
     if (more) {
@@ -315,21 +356,36 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
   // ---- epilogue: one division by the normaliser, one write of O.
   const float l_tot = halves_sum(l_lane);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (my_q < Nq) {
+  if (EPI == kEpiFinalBf16) {
+    // O in bf16 through LDS (free after the loop's last barrier): each lane
+    // writes its row's 4-column pieces, then every store to memory is 16
+    // contiguous bytes of one row, 16 lanes per row.
+    constexpr int OP = 2 * D + 16;  // LDS row pitch of the O block
+    char* orow = smem + (wave * 32 + r32) * OP;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        f32x4 v = {oacc[db][4 * r] * inv, oacc[db][4 * r + 1] * inv, oacc[db][4 * r + 2] * inv,
+                   oacc[db][4 * r + 3] * inv};
+        *(bf16x4*)(orow + 2 * (32 * db + 8 * r + 4 * g)) = __builtin_convertvector(v, bf16x4);
+      }
+    if (p.lse && g == 0 && my_q < Nq)
+      p.lse[(int64_t)bh * Nq + my_q] =
+          l_tot > 0.f ? m_run * p.scale_abs + __log2f(l_tot) * 0.69314718055994530942f : -INFINITY;
+    __syncthreads();
+    constexpr int CPO = D / 8;  // 16-byte chunks per O row
+    uint16_t* ob = (uint16_t*)p.o + ((int64_t)bh * Nq + q0) * D;
+#pragma unroll
+    for (int n = 0; n < G::BM * CPO / G::THREADS; ++n) {
+      const int idx = n * G::THREADS + tid;
+      const int r = idx / CPO, ch = idx % CPO;
+      const u32x4 v = *(const u32x4*)(smem + r * OP + 16 * ch);
+      if (q0 + r < Nq) *(u32x4*)(ob + (int64_t)r * D + 8 * ch) = v;
+    }
+  } else if (my_q < Nq) {
     const int64_t row = (int64_t)bh * Nq + my_q;
-    if (EPI == kEpiFinalBf16) {
-      uint16_t* og = (uint16_t*)p.o + row * D;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          f32x4 v = {oacc[db][4 * r] * inv, oacc[db][4 * r + 1] * inv, oacc[db][4 * r + 2] * inv,
-                     oacc[db][4 * r + 3] * inv};
-          *(bf16x4*)(og + 32 * db + 8 * r + 4 * g) = __builtin_convertvector(v, bf16x4);
-        }
-      if (p.lse && g == 0)
-        p.lse[row] = l_tot > 0.f ? m_run * p.scale_abs + __log2f(l_tot) * 0.69314718055994530942f : -INFINITY;
-    } else if (EPI == kEpiMerge) {
+    if (EPI == kEpiMerge) {
       // Online-softmax merge with the accumulated state of this row ("Sequence
       // parallelism and ring attention", "Technical insight"): M = max(m_acc,
       // m_blk), w_x = l_x e^(m_x - M), O = (w_acc O_acc + w_blk O_blk) / (w_acc +
