@@ -119,7 +119,12 @@ template <int D, bool CAUSAL, bool QK16, bool PV8, int W, int BN>
 __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
   using G = Geo8<D, QK16, PV8, W, BN>;
   constexpr int QT = kQuantTile;
-  __shared__ __attribute__((aligned(16))) char smem[G::LDS];
+  constexpr int OPF = D * 4 + 16;  // LDS row pitch of the fp32 O block in the epilogue
+  // fp8 Q.K: the workgroup's Q codes (BM rows of D bytes) sit after the K/V
+  // stages for the whole kernel.
+  constexpr int QLDS = QK16 ? 0 : G::BM * D;
+  constexpr int SMEM = G::LDS + QLDS > G::BM * OPF ? G::LDS + QLDS : G::BM * OPF;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -176,14 +181,29 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
         qf16[kk] = __builtin_bit_cast(f16x8, widen_lo((u32x4){cw[0], cw[1], 0u, 0u}));
       }
     } else {
-      const u32x4* src = (const u32x4*)(row + 32 * g);
+      // The Q block arrives by contiguous 1 KiB transfers into LDS (rows of D
+      // bytes; a row's 16-byte chunk c sits at slot c ^ ((r / (256 / D)) mod
+      // D/16), so the fragment reads of 16 consecutive rows at one chunk hit
+      // distinct banks); the fragments are read after the prologue's barrier.
+      // Transfer j covers rows (1024 / D) j ..; wavefront w issues j = w + 8n,
+      // which fixes each lane's row and chunk permutation.
+      constexpr int QR = 1024 / D, CPQ = D / 16, RPW = 256 / D;
+      const int rin = lane / CPQ, jc = lane % CPQ;
+      const int swz = ((QR * (wave & 1) + rin) / RPW) & (CPQ - 1);
+      const unsigned q_lane = (unsigned)(rin * D + 16 * (jc ^ swz));
+      const i32x4 rsrc = buffer_rsrc(qg + (int64_t)q0 * D);
+      unsigned lds = __builtin_amdgcn_readfirstlane(lds_offset(smem + G::LDS) + 1024u * wave);
+      if (q0 + G::BM <= Nq) {
+        unsigned soff = __builtin_amdgcn_readfirstlane(1024u * wave);
 #pragma unroll
-      for (int kk = 0; kk < QF; ++kk) {
-        u32x4 a = ok ? src[kk * 4] : (u32x4){0u, 0u, 0u, 0u};
-        u32x4 b = ok ? src[kk * 4 + 1] : (u32x4){0u, 0u, 0u, 0u};
-        a = (a & q_and) ^ sgn;
-        b = (b & q_and) ^ sgn;
-        qf8[kk] = (i32x8){(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+        for (int n = 0; n < G::BM * D / 1024 / W; ++n) buf_lds16<1024 * W, 1024 * W>(rsrc, q_lane, soff, lds);
+      } else {  // last block of a slice: rows past Nq read the last row
+        unsigned soff = 0;
+#pragma unroll 1
+        for (int j = wave; j < G::BM * D / 1024; j += W) {
+          const int r = min(q0 + QR * j + rin, Nq - 1) - q0;
+          buf_lds16<0, 1024 * W>(rsrc, (unsigned)(r * D) + (q_lane - (unsigned)(rin * D)), soff, lds);
+        }
       }
     }
   }
@@ -330,6 +350,26 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
     lstore_v(0);
   }
   publish();
+  if constexpr (!QK16) {
+    // Q fragment (B operand): row my_q, bytes 64 kk + 32 g .. +32 = chunks
+    // 4 kk + 2 g and 4 kk + 2 g + 1 of block row r = 32 wave + r32.
+    constexpr int CPQ = D / 16, RPW = 256 / D;
+    const int r = wave * 32 + r32;
+    const char* qrow = smem + G::LDS + r * D;
+    const int swz = (r / RPW) & (CPQ - 1);
+    const bool ok = my_q < Nq;
+    const uint32_t q_and = p.q_and ? 0xFFFFFFFFu : 0u;
+    const uint32_t sgn = p.q_xor ? 0x80808080u : 0u;
+#pragma unroll
+    for (int kk = 0; kk < QF; ++kk) {
+      u32x4 a = *(const u32x4*)(qrow + 16 * ((4 * kk + 2 * g) ^ swz));
+      u32x4 b = *(const u32x4*)(qrow + 16 * ((4 * kk + 2 * g + 1) ^ swz));
+      a = (a & q_and) ^ sgn;
+      b = (b & q_and) ^ sgn;
+      if (!ok) a = b = (u32x4){0u, 0u, 0u, 0u};
+      qf8[kk] = (i32x8){(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+    }
+  }
 
   for (int t = 0; t < ntiles; ++t) {
     const bool more = t + 1 < ntiles;
@@ -456,19 +496,31 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
 
   const float l_tot = halves_sum(l_lane);
   const float inv = l_tot > 0.f ? svmax / l_tot : 0.f;  // O = oacc * svmax / l
-  if (my_q < Nq) {
-    const int64_t row = (int64_t)bh * Nq + my_q;
-    float* og = (float*)p.o + row * D;
+  // O in fp32 through LDS (free after the loop's last barrier): each lane
+  // writes its row's 4-column pieces, then every store to memory is 16
+  // contiguous bytes of one row, D/4 lanes per row.
+  {
+    char* orow = smem + (wave * 32 + r32) * OPF;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         f32x4 v = {oacc[db][4 * r] * inv, oacc[db][4 * r + 1] * inv, oacc[db][4 * r + 2] * inv,
                    oacc[db][4 * r + 3] * inv};
-        *(f32x4*)(og + 32 * db + 8 * r + 4 * g) = v;
+        *(f32x4*)(orow + 4 * (32 * db + 8 * r + 4 * g)) = v;
       }
-    if (p.lse && g == 0)
-      p.lse[row] = l_tot > 0.f ? (m2 + __log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
+  }
+  if (p.lse && g == 0 && my_q < Nq)
+    p.lse[(int64_t)bh * Nq + my_q] = l_tot > 0.f ? (m2 + __log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
+  __syncthreads();
+  constexpr int CPO = D / 4;  // 16-byte chunks per O row
+  float* ob = (float*)p.o + ((int64_t)bh * Nq + q0) * D;
+#pragma unroll
+  for (int n = 0; n < G::BM * CPO / G::THREADS; ++n) {
+    const int idx = n * G::THREADS + tid;
+    const int r = idx / CPO, ch = idx % CPO;
+    const f32x4 v = *(const f32x4*)(smem + r * OPF + 16 * ch);
+    if (q0 + r < Nq) *(f32x4*)(ob + (int64_t)r * D + 4 * ch) = v;
   }
 }
 
