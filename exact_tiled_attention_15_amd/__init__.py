@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     MFMA_PEAK_THREADS,
     W4A16_GROUP,
     W4A16_MAX_M,
+    W4A16_NOALLOC_MAX_WORK_FLOATS,
     W4A16_TOKENS_PER_PASS,
     AttnError,
     abi_version,
@@ -41,5 +42,6 @@ from ._lib import (  # noqa: F401
     ring_work_floats,
     status_str,
     w4a16_gemm,
+    w4a16_gemm_noalloc,
     w4a16_work_floats,
 )

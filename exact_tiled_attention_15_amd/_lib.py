@@ -21,6 +21,7 @@ FP8_TILE = 128
 W4A16_GROUP = 128
 W4A16_MAX_M = 4096
 W4A16_TOKENS_PER_PASS = 16
+W4A16_NOALLOC_MAX_WORK_FLOATS = 1 << 21
 MFMA_BF16, MFMA_F16, MFMA_FP8, MFMA_F32 = 0, 1, 2, 3
 MFMA_PEAK_THREADS = 512
 
@@ -77,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.w4a16_work_floats.argtypes = [i64, i64, i64, i64]
     L.w4a16_gemm.restype = i
     L.w4a16_gemm.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp]
+    L.w4a16_gemm_noalloc.restype = i
+    L.w4a16_gemm_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp]
     L.attn_mfma_peak_flop.restype = ctypes.c_double
     L.attn_mfma_peak_flop.argtypes = [i, i, i]
     L.attn_mfma_peak.restype = i
@@ -331,6 +334,21 @@ def w4a16_gemm(x, packed, scales, zeros, y, work=None, group: int = W4A16_GROUP,
         _want(work, torch.float32, (nw,), "work")
     _check(lib().w4a16_gemm(_ptr(x), _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(y),
                             _ptr(work) if nw else None, M, N, K, group, _stream(stream)), "w4a16_gemm")
+
+
+def w4a16_gemm_noalloc(x, packed, scales, zeros, y, group: int = W4A16_GROUP, stream=None):
+    """w4a16_gemm with its split partials in the library's fixed device array (no workspace)."""
+    M, K = x.shape
+    N = packed.shape[0]
+    if K % 8 or K % group:
+        raise ValueError("K must be a multiple of 8 and of the group size")
+    _want(x, torch.float16, (M, K), "x")
+    _want(packed, torch.int32, (N, K // 8), "packed")
+    _want(scales, torch.float16, (N, K // group), "scales")
+    _want(zeros, torch.uint8, (N, K // group), "zeros")
+    _want(y, torch.float16, (M, N), "y")
+    _check(lib().w4a16_gemm_noalloc(_ptr(x), _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(y), M, N, K, group,
+                                    _stream(stream)), "w4a16_gemm_noalloc")
 
 
 def mfma_peak_flop(kind: int, workgroups: int, iters: int) -> float:

@@ -486,14 +486,15 @@ size_t w4a16_work_floats(int64_t M, int64_t N, int64_t K, int64_t group) {
   return eta::w4a16_plan(std::min<int64_t>(M, W4A16_TOKENS_PER_PASS), N, K).work_floats;
 }
 
-attn_status w4a16_gemm(const void* x, const uint32_t* packed, const void* scales, const uint8_t* zeros, void* y,
-                       float* work, int64_t M, int64_t N, int64_t K, int64_t group, void* stream) {
-  if (attn_status s = check_w4a16(M, N, K, group)) return s;
-  if (attn_status s = check_ptrs16({x, packed})) return s;
-  if (!scales || !aligned(scales, 2) || !zeros || !y || !aligned(y, 2)) return ATTN_ERR_INVALID;
-  const int64_t mp = std::min<int64_t>(M, W4A16_TOKENS_PER_PASS);
-  const eta::W4Plan pl = eta::w4a16_plan(mp, N, K);  // the same plan for every pass
-  if (pl.work_floats && (!work || !aligned(work, 4))) return ATTN_ERR_INVALID;
+}  // extern "C"
+
+namespace {
+
+// The passes of one W4A16 call (arguments already validated; work holds
+// pl.work_floats floats when pl.work_floats > 0).
+attn_status run_w4a16(const void* x, const uint32_t* packed, const void* scales, const uint8_t* zeros, void* y,
+                      float* work, const eta::W4Plan& pl, int64_t M, int64_t N, int64_t K, int64_t group,
+                      void* stream) {
   const int cu = device_compute_units();
   // One pass per block of up to 16 tokens, in order on the caller's stream
   // (passes reuse the workspace one after another).
@@ -512,6 +513,37 @@ attn_status w4a16_gemm(const void* x, const uint32_t* packed, const void* scales
     if (attn_status s = from_hip(eta::launch_w4a16(p, pl, cu > 0 ? cu : 256, (hipStream_t)stream))) return s;
   }
   return ATTN_OK;
+}
+
+attn_status check_w4a16_ptrs(const void* x, const uint32_t* packed, const void* scales, const uint8_t* zeros,
+                             const void* y) {
+  if (attn_status s = check_ptrs16({x, packed})) return s;
+  if (!scales || !aligned(scales, 2) || !zeros || !y || !aligned(y, 2)) return ATTN_ERR_INVALID;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status w4a16_gemm(const void* x, const uint32_t* packed, const void* scales, const uint8_t* zeros, void* y,
+                       float* work, int64_t M, int64_t N, int64_t K, int64_t group, void* stream) {
+  if (attn_status s = check_w4a16(M, N, K, group)) return s;
+  if (attn_status s = check_w4a16_ptrs(x, packed, scales, zeros, y)) return s;
+  const eta::W4Plan pl = eta::w4a16_plan(std::min<int64_t>(M, W4A16_TOKENS_PER_PASS), N, K);
+  if (pl.work_floats && (!work || !aligned(work, 4))) return ATTN_ERR_INVALID;
+  return run_w4a16(x, packed, scales, zeros, y, work, pl, M, N, K, group, stream);
+}
+
+attn_status w4a16_gemm_noalloc(const void* x, const uint32_t* packed, const void* scales, const uint8_t* zeros,
+                               void* y, int64_t M, int64_t N, int64_t K, int64_t group, void* stream) {
+  if (attn_status s = check_w4a16(M, N, K, group)) return s;
+  if (attn_status s = check_w4a16_ptrs(x, packed, scales, zeros, y)) return s;
+  const eta::W4Plan pl = eta::w4a16_plan(std::min<int64_t>(M, W4A16_TOKENS_PER_PASS), N, K);
+  if (pl.work_floats > W4A16_NOALLOC_MAX_WORK_FLOATS) return ATTN_ERR_UNSUPPORTED;
+  float* work = nullptr;
+  if (pl.work_floats && eta::w4a16_scratch(&work) != hipSuccess) return ATTN_ERR_HIP;
+  return run_w4a16(x, packed, scales, zeros, y, work, pl, M, N, K, group, stream);
 }
 
 double attn_mfma_peak_flop(int kind, int workgroups, int iters) {

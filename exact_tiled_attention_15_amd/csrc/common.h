@@ -243,5 +243,8 @@ struct W4Plan {
 };
 W4Plan w4a16_plan(int64_t M, int64_t N, int64_t K);
 hipError_t launch_w4a16(const W4Params& p, const W4Plan& pl, int compute_units, hipStream_t s);
+// Device address of the fixed split-partial array of w4a16_gemm_noalloc on
+// the current device (W4A16_NOALLOC_MAX_WORK_FLOATS floats).
+hipError_t w4a16_scratch(float** out);
 
 }  // namespace eta

@@ -38,9 +38,45 @@
 #include <algorithm>
 #include <type_traits>
 
+#include <atomic>
+#include <mutex>
+
 #include "common.h"
+#include "w4a16.h"
+
+// Split partials of w4a16_gemm_noalloc: a fixed device array, one copy per
+// GPU, held until the process ends.  Host code never passes this name to a
+// kernel (on the host it is only a stand-in for the symbol): the device
+// address comes from w4a16_scratch below.
+static __device__ __align__(256) float scratch[W4A16_NOALLOC_MAX_WORK_FLOATS];
 
 namespace eta {
+
+// Device address of `scratch` on the current device, looked up once per device
+// (hipGetSymbolAddress with that device current) and kept.
+hipError_t w4a16_scratch(float** out) {
+  constexpr int kDevices = 64;
+  static std::atomic<float*> ptrs[kDevices];
+  static std::mutex mu;
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return e;
+  if (dev < 0 || dev >= kDevices) return hipErrorInvalidDevice;
+  float* p = ptrs[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = ptrs[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* a = nullptr;
+      if (hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch))) return e;
+      if (!a) return hipErrorInvalidSymbol;
+      p = static_cast<float*>(a);
+      ptrs[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
 namespace {
 
 constexpr int kW4Waves = 8;

@@ -72,6 +72,29 @@ attn_status w4a16_gemm(const void* x, const uint32_t* packed, const void* scales
                        const uint8_t* zeros, void* y, float* work, int64_t M, int64_t N,
                        int64_t K, int64_t group, void* stream);
 
+/* Largest split workspace (fp32 elements, 8 MiB) that w4a16_gemm_noalloc
+ * holds in its fixed device array. */
+#define W4A16_NOALLOC_MAX_WORK_FLOATS (1u << 21)
+
+/*
+ * w4a16_gemm_noalloc - w4a16_gemm for callers that cannot allocate device
+ * memory or pass a workspace (code under stream capture, tight decode loops,
+ * harnesses that forbid allocation).  Same arguments, layout, result (bit
+ * for bit) and errors as w4a16_gemm, without `work`: the split partials go to
+ * a fixed device array of W4A16_NOALLOC_MAX_WORK_FLOATS floats that the
+ * library keeps on each GPU it runs on until the process ends.  Calls whose
+ * w4a16_work_floats exceeds that limit return ATTN_ERR_UNSUPPORTED and
+ * enqueue nothing; calls that need no split do not touch the array.  The
+ * call allocates nothing (its first call on a device looks up the array's
+ * device address once).  Every call on one GPU shares the one array, so
+ * calls that may overlap on the same GPU (different streams, or host threads
+ * without ordering) race and give undefined results; calls ordered on one
+ * stream are safe.  ATTN_ERR_HIP if the array's address cannot be obtained.
+ */
+attn_status w4a16_gemm_noalloc(const void* x, const uint32_t* packed, const void* scales,
+                               const uint8_t* zeros, void* y, int64_t M, int64_t N, int64_t K,
+                               int64_t group, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
