@@ -24,6 +24,7 @@ from ._lib import (  # noqa: F401
     AttnError,
     abi_version,
     attn_bwd,
+    attn_fwd_block_order,
     attn_fwd,
     attn_fwd_f32,
     attn_fwd_fp8,

@@ -1,4 +1,4 @@
-"""ctypes binding of libattn.so (include/attn.h, include/w4a16.h, include/mfma_probe.h).
+"""ctypes binding of libattn.so (include/attn.h, attn_diag.h, w4a16.h, mfma_probe.h).
 
 Argument marshalling only: every function here checks that the torch tensors
 it is handed have the dtype/shape/device the C entry point documents, passes
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.w4a16_gemm.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp]
     L.w4a16_gemm_noalloc.restype = i
     L.w4a16_gemm_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp]
+    L.attn_fwd_block_order.restype = i
+    L.attn_fwd_block_order.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, ctypes.c_uint32, vp]
     L.attn_mfma_peak_flop.restype = ctypes.c_double
     L.attn_mfma_peak_flop.argtypes = [i, i, i]
     L.attn_mfma_peak.restype = i
@@ -349,6 +351,21 @@ def w4a16_gemm_noalloc(x, packed, scales, zeros, y, group: int = W4A16_GROUP, st
     _want(y, torch.float16, (M, N), "y")
     _check(lib().w4a16_gemm_noalloc(_ptr(x), _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(y), M, N, K, group,
                                     _stream(stream)), "w4a16_gemm_noalloc")
+
+
+def attn_fwd_block_order(q, k, v, o, lse, causal: bool, scale: float, order: int, stream=None):
+    """attn_fwd with the workgroup -> tile assignment permuted by `order` (diagnostic)."""
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    _want(q, torch.bfloat16, (B, H, Nq, d), "q")
+    _want(k, torch.bfloat16, (B, H, Nk, d), "k")
+    _want(v, torch.bfloat16, (B, H, Nk, d), "v")
+    _want(o, torch.bfloat16, (B, H, Nq, d), "o")
+    if lse is not None:
+        _want(lse, torch.float32, (B, H, Nq), "lse")
+    _check(lib().attn_fwd_block_order(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
+                                      int(bool(causal)), float(scale), int(order), _stream(stream)),
+           "attn_fwd_block_order")
 
 
 def mfma_peak_flop(kind: int, workgroups: int, iters: int) -> float:

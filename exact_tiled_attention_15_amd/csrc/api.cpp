@@ -4,6 +4,7 @@
 // The one HIP object the library creates itself is attn_fwd_ring_host's copy
 // stream (with its events), once per device.
 #include "attn.h"
+#include "attn_diag.h"
 #include "mfma_probe.h"
 #include "w4a16.h"
 
@@ -285,6 +286,31 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   p.v = v;
   p.o = o;
   p.lse = lse;
+  return from_hip(eta::launch_fwd_bf16(p, d, causal != 0, eta::kEpiFinalBf16, (hipStream_t)stream));
+}
+
+attn_status attn_fwd_block_order(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                                 int Nq, int Nk, int d, int causal, float scale, uint32_t order, void* stream) {
+  if (attn_status s = check_shape(B, H, Nq, Nk, d)) return s;
+  if (attn_status s = check_ptrs16({q, k, v, o})) return s;
+  if (attn_status s = check_ptrs4({lse}, true)) return s;
+  if (!std::isfinite(scale)) return ATTN_ERR_INVALID;
+  FwdParams p = base_params(B, H, Nq, Nk, scale);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  if (order != 0) {
+    // grid size of the bf16 forward: one workgroup per (b, h, 256-row block)
+    const uint64_t n = uint64_t(B) * H * ((uint64_t(Nq) + 255) / 256);
+    uint64_t mul = (uint64_t(order) * 2654435761u) % n;
+    if (mul == 0) mul = 1;
+    auto gcd = [](uint64_t a, uint64_t b) { while (b) { const uint64_t t = a % b; a = b; b = t; } return a; };
+    while (gcd(mul, n) != 1) mul = mul + 1 < n ? mul + 1 : 1;
+    p.perm_mul = uint32_t(mul);
+    p.perm_add = uint32_t((uint64_t(order) * 40503u) % n);
+  }
   return from_hip(eta::launch_fwd_bf16(p, d, causal != 0, eta::kEpiFinalBf16, (hipStream_t)stream));
 }
 

@@ -67,7 +67,18 @@ struct FwdParams {
   // when scale == 0 (all scores 0, the same problem as Q = 0).
   uint32_t q_and;
   uint32_t q_xor;
+  // Workgroup order: workgroup g computes the tile of index (g * perm_mul +
+  // perm_add) mod grid (perm_mul coprime to the grid size, so a bijection);
+  // perm_mul = 0 is the identity.  Only the diagnostic entry point sets it.
+  uint32_t perm_mul;
+  uint32_t perm_add;
 };
+
+// Tile index of this workgroup under the FwdParams workgroup order.
+__device__ inline int tile_index(const FwdParams& p) {
+  if (p.perm_mul == 0) return blockIdx.x;
+  return (int)(((uint64_t)blockIdx.x * p.perm_mul + p.perm_add) % gridDim.x);
+}
 
 // Launchers (host side). Each returns hipGetLastError() after the launch.
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, int epi, hipStream_t s);

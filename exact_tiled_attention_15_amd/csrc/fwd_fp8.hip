@@ -133,7 +133,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
   const int g = lane >> 5;
 
   int qb, bh;
-  map_block(blockIdx.x, p.nqb, p.BH, CAUSAL, qb, bh);
+  map_block(tile_index(p), p.nqb, p.BH, CAUSAL, qb, bh);
   const int q0 = qb * G::BM;
   const int qw0 = q0 + wave * 32;
   const int my_q = qw0 + r32;

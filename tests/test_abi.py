@@ -34,7 +34,8 @@ def test_library_exports_every_declared_function():
     names = declared_functions()
     assert {"attn_fwd", "attn_fwd_f32", "attn_fwd_kvblock", "attn_merge", "attn_fwd_fp8",
             "attn_abi_version", "attn_status_str", "w4a16_gemm", "w4a16_work_floats",
-            "attn_mfma_peak", "attn_mfma_dot", "attn_mfma_peak_flop"} <= set(names)
+            "attn_mfma_peak", "attn_mfma_dot", "attn_mfma_peak_flop", "attn_fwd_block_order",
+            "w4a16_gemm_noalloc"} <= set(names)
     L = eta.lib()
     for n in names:
         assert hasattr(L, n), f"{n} not exported by libattn.so"

@@ -92,6 +92,26 @@ def test_deterministic_and_every_output_written():
         assert torch.equal(lse.view(torch.int32), outs[0][1].view(torch.int32))
 
 
+@pytest.mark.parametrize("B,H,N,causal", [(2, 4, 777, True), (8, 16, 2048, True), (1, 3, 1000, False)])
+def test_deterministic_under_permuted_workgroup_order(B, H, N, causal):
+    """Exact and deterministic ("FlashAttention-2", "Performance and efficiency"): the same output,
+    bit for bit, whichever workgroup computes which (b, h, query block) tile."""
+    say(f"workgroup order B={B} H={H} N={N} causal={causal}")
+    qb, kb, vb = _bf16_problem(B, H, N, N, 128, 123 + N)
+    q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    o0 = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    l0 = torch.full(q.shape[:3], float("nan"), device="cuda")
+    eta.attn_fwd(q, k, v, o0, l0, causal, 0.0884)
+    for order in (1, 7, 12345, 2**31 + 5):
+        o = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full(q.shape[:3], float("nan"), device="cuda")
+        eta.attn_fwd_block_order(q, k, v, o, lse, causal, 0.0884, order)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o0.view(torch.int16)), f"order {order}: O differs"
+        assert torch.equal(lse.view(torch.int32), l0.view(torch.int32)), f"order {order}: LSE differs"
+    assert not torch.isnan(o0).any() and not torch.isnan(l0).any()
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_zero_query_gives_prefix_mean(causal):
     say(f"zero query causal={causal}")
