@@ -324,10 +324,15 @@ def main():
         t = {n: dv(x[n]) for n in ("q8", "k8", "v8", "q_scale", "k_scale", "v_scale")}
         o = torch.empty((B, H, Nq, d), device="cuda")
         lse = torch.empty((B, H, Nq), device="cuda")
-        fp8_fn = (eta.attn_fwd_fp8_pv8 if cfg.get("pv8") else
-                  eta.attn_fwd_fp8_qk16 if cfg.get("qk16") else eta.attn_fwd_fp8)
-        step = lambda: fp8_fn(t["q8"], t["k8"], t["v8"], t["q_scale"], t["k_scale"], t["v_scale"],
-                              o, lse, causal, scale, stream)
+        if cfg.get("pv4"):
+            direct = bool(cfg.get("direct_p"))
+            step = lambda: eta.attn_fwd_fp8_pv4(t["q8"], t["k8"], t["v8"], t["q_scale"], t["k_scale"],
+                                                t["v_scale"], o, lse, causal, scale, direct, stream)
+        else:
+            fp8_fn = (eta.attn_fwd_fp8_pv8 if cfg.get("pv8") else
+                      eta.attn_fwd_fp8_qk16 if cfg.get("qk16") else eta.attn_fwd_fp8)
+            step = lambda: fp8_fn(t["q8"], t["k8"], t["v8"], t["q_scale"], t["k_scale"], t["v_scale"],
+                                  o, lse, causal, scale, stream)
         kernel = "fwd_fp8_kernel"
         launches = 1
 

@@ -28,6 +28,7 @@ from ._lib import (  # noqa: F401
     attn_fwd,
     attn_fwd_f32,
     attn_fwd_fp8,
+    attn_fwd_fp8_pv4,
     attn_fwd_fp8_pv8,
     attn_fwd_fp8_qk16,
     attn_fwd_kvblock,

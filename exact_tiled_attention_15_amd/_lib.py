@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.restype = i
         fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    L.attn_fwd_fp8_pv4.restype = i
+    L.attn_fwd_fp8_pv4.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     L.w4a16_work_floats.restype = ctypes.c_size_t
     L.w4a16_work_floats.argtypes = [i64, i64, i64, i64]
     L.w4a16_gemm.restype = i
@@ -276,7 +278,7 @@ def attn_fwd_ring_host(q, k_blks, v_blks, k_pos, o, lse, work, stage, causal: bo
            "attn_fwd_ring_host")
 
 
-def _fwd_fp8(entry, q8, k8, v8, q_scale, k_scale, v_scale, o, lse, causal, scale, stream):
+def _fwd_fp8(entry, q8, k8, v8, q_scale, k_scale, v_scale, o, lse, causal, scale, stream, extra=()):
     B, H, Nq, d = q8.shape
     Nk = k8.shape[2]
     nqt = (Nq + FP8_TILE - 1) // FP8_TILE
@@ -292,7 +294,7 @@ def _fwd_fp8(entry, q8, k8, v8, q_scale, k_scale, v_scale, o, lse, causal, scale
         _want(lse, torch.float32, (B, H, Nq), "lse")
     fn = getattr(lib(), entry)
     _check(fn(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _ptr(o), _ptr(lse),
-              B, H, Nq, Nk, d, int(bool(causal)), float(scale), _stream(stream)), entry)
+              B, H, Nq, Nk, d, int(bool(causal)), float(scale), *extra, _stream(stream)), entry)
 
 
 def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, causal: bool, scale: float,
@@ -311,6 +313,14 @@ def attn_fwd_fp8_pv8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, causal: bool
                      stream=None):
     """As attn_fwd_fp8 with P in e4m3 and P.V on fp8 matrix cores (faster, drifts by P's rounding)."""
     _fwd_fp8("attn_fwd_fp8_pv8", q8, k8, v8, q_scale, k_scale, v_scale, o, lse, causal, scale, stream)
+
+
+def attn_fwd_fp8_pv4(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, causal: bool, scale: float,
+                     direct_p: bool = False, stream=None):
+    """As attn_fwd_fp8_pv8 with P as 4-bit e2m1 codes: each exponential rounded (direct_p False) or
+    the score mapped straight to the code (Direct-P)."""
+    _fwd_fp8("attn_fwd_fp8_pv4", q8, k8, v8, q_scale, k_scale, v_scale, o, lse, causal, scale, stream,
+             extra=(int(bool(direct_p)),))
 
 
 def w4a16_work_floats(M: int, N: int, K: int, group: int = W4A16_GROUP) -> int:

@@ -53,6 +53,15 @@ WORKLOADS = {
     "fp8_pv8_B4_H16_N4096_d128": dict(index=7, B=4, H=16, Nq=4096, Nk=4096, d=128, dtype="fp8",
                                       causal=False, outlier_frac=0.01, outlier_mult=20.0,
                                       oracle_rows=512, rotate=True, pv8=True),
+    # The same inputs with the probabilities as 4-bit e2m1 codes (P.V on the f8f6f4 matrix cores
+    # with V's e4m3 codes): each exponential rounded, and Direct-P (score mapped straight to the
+    # code).  Same seed as the e4m3-P workload, so the drifts compare on identical inputs.
+    "fp8_pv4_B4_H16_N4096_d128": dict(index=7, B=4, H=16, Nq=4096, Nk=4096, d=128, dtype="fp8",
+                                      causal=False, outlier_frac=0.01, outlier_mult=20.0,
+                                      oracle_rows=512, rotate=True, pv4=True),
+    "fp8_directp_B4_H16_N4096_d128": dict(index=7, B=4, H=16, Nq=4096, Nk=4096, d=128, dtype="fp8",
+                                          causal=False, outlier_frac=0.01, outlier_mult=20.0,
+                                          oracle_rows=512, rotate=True, pv4=True, direct_p=True),
     # W4A16 linear layers of token-by-token decoding ("Scaling FlashAttention, multi-GPU
     # training and weight quantization", section 3: a 70-billion-parameter model whose
     # weights, not its arithmetic, bound each generated token).  The two shapes of a

@@ -507,6 +507,14 @@ attn_status attn_fwd_fp8_pv8(const uint8_t* q8, const uint8_t* k8, const uint8_t
                  eta::kFp8AllFp8);
 }
 
+attn_status attn_fwd_fp8_pv4(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
+                             const float* k_scale, const float* v_scale, float* o, float* lse, int B, int H,
+                             int Nq, int Nk, int d, int causal, float scale, int direct_p, void* stream) {
+  if (direct_p != 0 && direct_p != 1) return ATTN_ERR_INVALID;
+  return fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, Nq, Nk, d, causal, scale, stream,
+                 direct_p ? eta::kFp8PvFp4Direct : eta::kFp8PvFp4);
+}
+
 size_t w4a16_work_floats(int64_t M, int64_t N, int64_t K, int64_t group) {
   if (check_w4a16(M, N, K, group) != ATTN_OK) return 0;
   return eta::w4a16_plan(std::min<int64_t>(M, W4A16_TOKENS_PER_PASS), N, K).work_floats;

@@ -84,8 +84,9 @@ __device__ inline int tile_index(const FwdParams& p) {
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, int epi, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t s);
 // fp8 forward modes: QK^T on fp8 or fp16 matrix cores (P.V on fp16), or both
-// products on fp8 matrix cores.
-enum Fp8Mode : int { kFp8QkFp8 = 0, kFp8QkFp16 = 1, kFp8AllFp8 = 2 };
+// products on f8f6f4 matrix cores with P in e4m3, or P in e2m1 (rounded
+// exponential, or Direct-P: score mapped straight to the code).
+enum Fp8Mode : int { kFp8QkFp8 = 0, kFp8QkFp16 = 1, kFp8AllFp8 = 2, kFp8PvFp4 = 3, kFp8PvFp4Direct = 4 };
 hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, int mode, hipStream_t s);
 
 struct MergeParams {

@@ -35,6 +35,19 @@
 //     mantissa bits, so this trades accuracy for speed: the result drifts from
 //     exact attention by the rounding of P (measured, not held to the parity
 //     bar).
+//   * PV4 instantiations (the FP4 probabilities of "Hardware-Aware FP4
+//     FlashAttention-4", gist.science summary): P.V on the same f8f6f4 MFMA
+//     with P as 4-bit e2m1 codes (B operand) against V's e4m3 codes (A).  P
+//     is quantized as 4 p s_v(t) / max s_v (<= 4) and the block scale 2^-2
+//     on P undoes the factor.  Either the exponential is rounded by the
+//     hardware conversion (nearest even), or - Direct-P - the score's base-2
+//     exponent relative to the running maximum is mapped straight to the code
+//     index with no exponential (index = clamp(round(2 log2(4 p) + 2), 0, 6),
+//     which matches nearest-even rounding of 4p from 0.59 up and flushes
+//     smaller values to 0).  With a 4-bit B operand the instruction takes k
+//     = 16g .. 16g+15 and 32+16g .. 32+16g+15 from lane half g (measured), so
+//     V^T uses its own key order (vt4_slot).  The normaliser sums the decoded
+//     codes.  One mantissa bit: a speed-for-accuracy mode, drift measured.
 //   * O accumulates and is written in fp32.
 // For the f8f6f4 MFMA the A/B k-slice of lane l is bytes (l/32)*32 .. +32.
 #include "common.h"
@@ -42,6 +55,11 @@
 namespace eta {
 
 constexpr int kQuantTile = 128;  // tokens per quantization tile
+
+// How P.V runs: fp16 P against fp16-widened V codes, or P in e4m3 / e2m1
+// against V's e4m3 codes on the f8f6f4 MFMA (e2m1 by rounding the exponential,
+// or by mapping the score straight to the code: Direct-P).
+enum PvMode : int { kPvF16 = 0, kPvFp8 = 1, kPvFp4 = 2, kPvFp4Direct = 3 };
 
 template <int D, bool QK16, bool PV8, int W, int BN>
 struct Geo8 {
@@ -69,6 +87,7 @@ struct Geo8 {
 };
 
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 
 __device__ inline u32x4 widen_lo(const u32x4 w) {  // codes 0..7 of 16 -> fp16
   u32x4 r;
@@ -97,10 +116,36 @@ __host__ __device__ constexpr int vt8_slot(int k) {
   return 64 * (k >> 6) + 32 * ((k >> 2) & 1) + 16 * ((k >> 5) & 1) + 4 * ((k >> 3) & 3) + (k & 3);
 }
 
+// Two fp32 values into e2m1 codes (nearest even) at byte `sel` of old, and
+// the two codes of byte `sel` back to fp32 (sel is a constant once unrolled).
+__device__ inline uint32_t pk_fp4(uint32_t old, float a, float b, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 3);
+  }
+}
+__device__ inline float2_t unpk_fp4(uint32_t w, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  }
+}
+
+// The same for a 4-bit P operand: lane half g of the B operand holds keys
+// 32b + 8(i/4) + 4g + i%4 (element i of block b) at k = 32b + 16g + i.
+__host__ __device__ constexpr int vt4_slot(int k) {
+  return 64 * (k >> 6) + 32 * ((k >> 5) & 1) + 16 * ((k >> 2) & 1) + 4 * ((k >> 3) & 3) + (k & 3);
+}
+
 // Four keys x 8 codes (w[r] = codes of key 4kg + r, columns d0 .. d0+7) into
 // fp8 V^T rows d0 .. d0+7: one 4-byte word per row (bytes = keys 4kg .. +3).
+template <bool P4>
 __device__ inline void store_vt8(char* vt, int pitch, int d0, int kg, const u32x2 (&w)[4]) {
-  const int col = vt8_slot(4 * kg);
+  const int col = P4 ? vt4_slot(4 * kg) : vt8_slot(4 * kg);
 #pragma unroll
   for (int hw = 0; hw < 2; ++hw) {  // codes 0..3 / 4..7 of each key
     const uint32_t k0 = w[0][hw], k1 = w[1][hw], k2 = w[2][hw], k3 = w[3][hw];
@@ -115,8 +160,10 @@ __device__ inline void store_vt8(char* vt, int pitch, int d0, int kg, const u32x
   }
 }
 
-template <int D, bool CAUSAL, bool QK16, bool PV8, int W, int BN>
+template <int D, bool CAUSAL, bool QK16, int PVM, int W, int BN>
 __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
+  constexpr bool PV8 = PVM != kPvF16;  // P.V on the f8f6f4 MFMA with V's codes
+  constexpr bool P4 = PVM == kPvFp4 || PVM == kPvFp4Direct;
   using G = Geo8<D, QK16, PV8, W, BN>;
   constexpr int QT = kQuantTile;
   constexpr int OPF = D * 4 + 16;  // LDS row pitch of the fp32 O block in the epilogue
@@ -285,7 +332,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
   auto lstore_v = [&](int t) {
     if (!v_stager) return;
     if constexpr (PV8) {
-      store_vt8(vstage(t), G::VTP8, 8 * v_dc, v_kg, vreg);
+      store_vt8<P4>(vstage(t), G::VTP8, 8 * v_dc, v_kg, vreg);
       return;
     }
     u32x4 w[4];
@@ -407,7 +454,54 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
       // P' = p * s_v(t) / s_v_max: the tile's V scale rides in the exponent
       // bias; the normaliser gets p back through one multiply per tile.
       const float bias_v = ((m2 == -INFINITY) ? 0.f : -m2) + vfold;
-      if constexpr (PV8) {
+      if constexpr (P4) {
+        // 4 P' in e2m1 and O^T += V^T P'^T on the f8f6f4 MFMA (B operand
+        // 4-bit), one 64-key group at a time.  Nibble t of the lane's B
+        // operand is element t % 16 of block 2 grp + t / 16 (k = 32 (t / 16)
+        // + 16 g + t % 16).  The normaliser sums the decoded codes.
+        float rs[4] = {0.f, 0.f, 0.f, 0.f};
+        const float bias4 = bias_v + 2.f;               // exp path: 4 P'
+        const float zc = 2.f * c, zb = 2.f * bias_v + 6.f;  // Direct-P: 2 log2(4 P') + 2
+#pragma unroll
+        for (int grp = 0; grp < G::KB / 2; ++grp) {
+          i32x8 pb4 = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int d2 = 0; d2 < 2; ++d2) {  // dword 2b + d2 = elements 8 d2 .. 8 d2 + 7 of block 2 grp + b
+              const f32x16& sv = s[2 * grp + b];
+              uint32_t w = 0;
+#pragma unroll
+              for (int pr = 0; pr < 4; ++pr) {
+                const int i0 = 8 * d2 + 2 * pr;
+                if constexpr (PVM == kPvFp4) {
+                  const float e0 = fast_exp2(fmaf(sv[i0], c, bias4)), e1 = fast_exp2(fmaf(sv[i0 + 1], c, bias4));
+                  w = pk_fp4(w, e0, e1, pr);
+                } else {
+                  const float z0 = __builtin_amdgcn_fmed3f(__builtin_rintf(fmaf(sv[i0], zc, zb)), 0.f, 6.f);
+                  const float z1 = __builtin_amdgcn_fmed3f(__builtin_rintf(fmaf(sv[i0 + 1], zc, zb)), 0.f, 6.f);
+                  w |= ((uint32_t)z0 | ((uint32_t)z1 << 4)) << (8 * pr);
+                }
+              }
+              pb4[2 * b + d2] = (int)w;
+#pragma unroll
+              for (int pr = 0; pr < 4; ++pr) {
+                const float2_t dv = unpk_fp4(w, pr);
+                rs[pr] += dv[0] + dv[1];
+              }
+            }
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const char* ap = vstage(t) + (32 * db + r32) * G::VTP8 + 64 * grp + 32 * g;
+            const u32x4 a0 = *(const u32x4*)ap;
+            const u32x4 a1 = *(const u32x4*)(ap + 16);
+            const i32x8 av = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                              (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+            oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb4, oacc[db], 0, 4, 0, 127, 0, 125);
+          }
+        }
+        l_lane += ((rs[0] + rs[1]) + (rs[2] + rs[3])) * (vunfold * 0.25f);
+      } else if constexpr (PV8) {
         // P' * 2^8 in e4m3 and O^T += V^T P'^T on the f8f6f4 MFMA, one 64-key
         // group at a time (4 MFMAs per group at d = 128).  The normaliser
         // sums the rounded values (2^-8 applied once per tile).
@@ -524,24 +618,26 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
   }
 }
 
-template <int D, bool QK16, bool PV8>
+template <int D, bool QK16, int PVM>
 static hipError_t launch_fp8_d(FwdParams p, bool causal, hipStream_t s) {
   constexpr int W = kWavesBf16, BN = kTileBf16;
   p.nqb = (p.Nq + 32 * W - 1) / (32 * W);
   const dim3 grid((unsigned)(p.nqb * p.BH));
   if (causal)
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, true, QK16, PV8, W, BN>), grid, dim3(64 * W), 0, s, p);
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, true, QK16, PVM, W, BN>), grid, dim3(64 * W), 0, s, p);
   else
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, false, QK16, PV8, W, BN>), grid, dim3(64 * W), 0, s, p);
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, false, QK16, PVM, W, BN>), grid, dim3(64 * W), 0, s, p);
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_fp8_mode(const FwdParams& p, bool causal, int mode, hipStream_t s) {
   switch (mode) {
-    case kFp8QkFp8: return launch_fp8_d<D, false, false>(p, causal, s);
-    case kFp8QkFp16: return launch_fp8_d<D, true, false>(p, causal, s);
-    case kFp8AllFp8: return launch_fp8_d<D, false, true>(p, causal, s);
+    case kFp8QkFp8: return launch_fp8_d<D, false, kPvF16>(p, causal, s);
+    case kFp8QkFp16: return launch_fp8_d<D, true, kPvF16>(p, causal, s);
+    case kFp8AllFp8: return launch_fp8_d<D, false, kPvFp8>(p, causal, s);
+    case kFp8PvFp4: return launch_fp8_d<D, false, kPvFp4>(p, causal, s);
+    case kFp8PvFp4Direct: return launch_fp8_d<D, false, kPvFp4Direct>(p, causal, s);
   }
   return hipErrorInvalidValue;
 }

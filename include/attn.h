@@ -283,6 +283,30 @@ attn_status attn_fwd_fp8_pv8(const uint8_t* q8, const uint8_t* k8, const uint8_t
                              float* o, float* lse, int B, int H, int Nq, int Nk, int d,
                              int causal, float scale, void* stream);
 
+/*
+ * attn_fwd_fp8_pv4 - as attn_fwd_fp8_pv8 with the probabilities as 4-bit
+ * e2m1 codes ("Hardware-Aware FP4 FlashAttention-4", gist.science summary:
+ * probabilities kept in the hardware's 4-bit format for the P.V product).
+ * P is quantized as 4 p s_v / max s_v (at most 4) and the matrix core's
+ * block scale 2^-2 undoes the factor; P.V runs on the f8f6f4 matrix cores
+ * with V's e4m3 codes; the normaliser sums the decoded codes.
+ *   direct_p = 0: each exponential is rounded to e2m1 (nearest even).
+ *   direct_p = 1: Direct-P: the score's base-2 exponent relative to the
+ *     running maximum is mapped straight to the code index (no
+ *     exponential): index = clamp(round(2 log2(4 p') + 2), 0, 6), which
+ *     matches nearest-even rounding for 4 p' >= 0.59 and flushes smaller
+ *     values to 0.
+ * e2m1 has one mantissa bit and nothing below 0.5 but 0: probabilities
+ * below 1/16 (1/8 rounded) of the row maximum vanish and the others move by
+ * up to 1/3; a speed-for-accuracy mode whose drift is measured, not held to
+ * the parity bar.  Same arguments and errors as attn_fwd_fp8, plus
+ * ATTN_ERR_INVALID for direct_p other than 0 or 1.
+ */
+attn_status attn_fwd_fp8_pv4(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                             const float* q_scale, const float* k_scale, const float* v_scale,
+                             float* o, float* lse, int B, int H, int Nq, int Nk, int d,
+                             int causal, float scale, int direct_p, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
