@@ -51,8 +51,11 @@ attn_status check_ptrs4(std::initializer_list<const void*> ps, bool nullable) {
   return ATTN_OK;
 }
 
+int device_compute_units();
+
 FwdParams base_params(int B, int H, int Nq, int Nk, float scale) {
   FwdParams p{};
+  p.ncu = device_compute_units();
   p.Nq = Nq;
   p.Nk = Nk;
   p.BH = B * H;

@@ -72,12 +72,38 @@ struct FwdParams {
   // perm_mul = 0 is the identity.  Only the diagnostic entry point sets it.
   uint32_t perm_mul;
   uint32_t perm_add;
+  // Compute units of the device (0 if unknown): persistent kernels launch at
+  // most this many workgroups.
+  int ncu;
 };
 
 // Tile index of this workgroup under the FwdParams workgroup order.
 __device__ inline int tile_index(const FwdParams& p) {
   if (p.perm_mul == 0) return blockIdx.x;
   return (int)(((uint64_t)blockIdx.x * p.perm_mul + p.perm_add) % gridDim.x);
+}
+// The same order applied to block g of n (persistent kernels, which walk
+// several blocks per workgroup).
+__device__ inline int block_perm(const FwdParams& p, int g, int n) {
+  if (p.perm_mul == 0) return g;
+  return (int)(((uint64_t)g * p.perm_mul + p.perm_add) % (uint64_t)n);
+}
+
+// Persistent schedule: the k-th block (in map_block's numbering) of workgroup
+// w of a grid of G, or -1 when it has no k-th block.  Rounds alternate
+// direction (snake order), so with blocks numbered heaviest first every
+// workgroup gets a near-equal share of tiles.  When G and n are multiples of
+// 8, workgroup w only takes blocks g with g % 8 == w % 8: the workgroups on
+// one XCD share that XCD's slices, and their K/V stays in its L2.  Every block
+// goes to exactly one workgroup.
+__device__ inline int sched_block(int k, int w, int G, int n) {
+  if ((G & 7) == 0 && (n & 7) == 0) {
+    const int x = w & 7, i = w >> 3, gx = G >> 3;
+    const int t = k * gx + ((k & 1) ? gx - 1 - i : i);
+    return t < (n >> 3) ? 8 * t + x : -1;
+  }
+  const int r = k * G + ((k & 1) ? G - 1 - w : w);
+  return r < n ? r : -1;
 }
 
 // Launchers (host side). Each returns hipGetLastError() after the launch.
@@ -176,6 +202,12 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline void load_lds16(const void* src, unsigned lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(src) : "memory", "m0");
 }
+// The same transfer from a wave-uniform base plus a 32-bit per-lane byte
+// offset (scalar-base form: no 64-bit lane address, so no VGPR pair).
+__device__ inline void load_lds16_s(const void* sbase, unsigned voff, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
 
 // Wave-wide global->LDS transfers through a buffer resource: 16 bytes per lane
 // from rsrc.base + soff + voff into LDS at lds + 16 * lane; soff and lds then
@@ -199,6 +231,13 @@ __device__ inline i32x4 buffer_rsrc(const void* base) {
   i32x4 r = {(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), -1, 0x00020000};
   r[0] = __builtin_amdgcn_readfirstlane(r[0]);
   r[1] = __builtin_amdgcn_readfirstlane(r[1]);
+  return r;
+}
+// The same with a range: accesses at byte offsets >= nbytes read as zero and
+// never touch memory (raw buffer, no swizzle).
+__device__ inline i32x4 buffer_rsrc_n(const void* base, unsigned nbytes) {
+  i32x4 r = buffer_rsrc(base);
+  r[2] = (int)__builtin_amdgcn_readfirstlane(nbytes);
   return r;
 }
 __device__ inline unsigned lds_offset(const void* x) {

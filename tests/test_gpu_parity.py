@@ -58,6 +58,32 @@ def test_attn_fwd_small_shapes(B, H, Nq, Nk, d, causal):
     compare_lse(lse, rl, "LSE")
 
 
+# More 256-row blocks than a chip has compute units: each workgroup of the
+# persistent forward walks two or more blocks, the next block's first K/V tile
+# and Q rows loading during the previous block's last tile.  Ragged last
+# blocks, blocks with no allowed key (causal, Nq - Nk >= 256: rows with no key
+# get O = 0 and LSE = -inf), d = 64, and block counts that are and are not
+# multiples of 8 (per-XCD and plain schedules).
+SEVERAL_BLOCKS = [
+    (1, 160, 300, 300, 128, True), (1, 100, 600, 40, 128, True), (2, 65, 257, 257, 64, False),
+    (1, 264, 256, 129, 128, True), (3, 97, 512, 300, 128, False),
+]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d,causal", SEVERAL_BLOCKS)
+def test_attn_fwd_several_blocks_per_workgroup(B, H, Nq, Nk, d, causal):
+    say(f"attn_fwd several blocks B={B} H={H} Nq={Nq} Nk={Nk} d={d} causal={causal}")
+    assert B * H * ((Nq + 255) // 256) > 256
+    seed = 11 + Nq * 5 + Nk * 3 + d + int(causal) + H
+    qb, kb, vb = _bf16_problem(B, H, Nq, Nk, d, seed)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = _run_fwd(qb, kb, vb, causal, scale)
+    ro, rl = oracle.attention(oracle.decode_bf16(qb), oracle.decode_bf16(kb), oracle.decode_bf16(vb),
+                              causal, scale)
+    compare_o(o, ro, BF16_BAR, "O")
+    compare_lse(lse, rl, "LSE")
+
+
 @pytest.mark.parametrize("Nq,Nk,d,causal", [(256, 256, 64, False), (200, 333, 128, True), (65, 31, 64, True)])
 def test_attn_fwd_f32_small(Nq, Nk, d, causal):
     say(f"attn_fwd_f32 Nq={Nq} Nk={Nk} d={d} causal={causal}")
