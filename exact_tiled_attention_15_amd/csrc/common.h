@@ -290,6 +290,7 @@ struct W4Params {
 // wavefront, ntiles 16-row tiles; work_floats = S * M * N when S > 1.
 struct W4Plan {
   int S, gps, gw, ntiles;
+  int nw;  // wavefronts per workgroup
   size_t work_floats;
 };
 W4Plan w4a16_plan(int64_t M, int64_t N, int64_t K);

@@ -128,17 +128,22 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 template <int GW>
 constexpr int ring_depth() { return GW == 8 ? 4 : GW == 6 ? 3 : GW; }
 
-template <int GW>
-__global__ __launch_bounds__(kW4Threads) void w4a16_kernel(W4Params p) {
+template <int GW, int NW>
+__global__ __launch_bounds__(64 * NW) void w4a16_kernel(W4Params p) {
   constexpr int D = ring_depth<GW>();
   static_assert(GW % D == 0, "ring depth must divide the slots per wavefront");
   constexpr int kTab = kW4MaxSplitGroups + 1;  // last column: zero scale for dead slots
-  __shared__ float xs[kW4Waves][GW][2][16];        // per token: X'g, Xg
-  __shared__ float red[2][kW4Waves][16][kW4Rows];  // per-wave partial tiles
+  __shared__ float xs[NW][GW][2][16];        // per token: X'g, Xg
+  // Per-wave partial tiles, row c of W (column of y) by token, each row padded
+  // to 20 floats: the 16-byte writes of a wavefront (4 tokens of one row per
+  // lane) and the reducing reads (16 rows of one token) both fall on distinct
+  // banks.
+  constexpr int kRedPitch = 20;
+  __shared__ float red[2][NW][kW4Rows][kRedPitch];
   __shared__ float2 sz[2][kW4Rows][kTab];          // per tile: (scale, zero point) of each group
   // Activation staging, one group per wavefront: 16 tokens x 16 chunks of
   // 16 B, rows padded by one chunk so the transposed reads are conflict-free.
-  __shared__ u32x4 xst[kW4Waves][16][17];
+  __shared__ u32x4 xst[NW][16][17];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -179,7 +184,7 @@ __global__ __launch_bounds__(kW4Threads) void w4a16_kernel(W4Params p) {
   bool e_live[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int e = threadIdx.x + j * kW4Threads;
+    const int e = threadIdx.x + j * (64 * NW);
     e_live[j] = e < kW4Rows * ngs;
     e_row[j] = e_live[j] ? e / ngs : 0;
     e_col[j] = e_live[j] ? e % ngs : 0;
@@ -307,8 +312,7 @@ __global__ __launch_bounds__(kW4Threads) void w4a16_kernel(W4Params p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red[par][wave][4 * quad + i][col] = acc[i];
+    *reinterpret_cast<f32x4*>(&red[par][wave][col][4 * quad]) = acc;
     park_sz(par ^ 1);  // the table of the next tile (its loads were issued a tile ago)
     issue_sz(next2);
     __syncthreads();
@@ -318,7 +322,7 @@ __global__ __launch_bounds__(kW4Threads) void w4a16_kernel(W4Params p) {
       if (m < p.M && n < p.N) {
         float sum = 0.f;
 #pragma unroll
-        for (int w2 = 0; w2 < kW4Waves; ++w2) sum += red[par][w2][m][c];
+        for (int w2 = 0; w2 < NW; ++w2) sum += red[par][w2][c][m];
         if (p.part)
           p.part[(int64_t(blockIdx.y) * p.M + m) * p.N + n] = sum;
         else
@@ -368,9 +372,9 @@ __global__ __launch_bounds__(256) void w4a16_reduce_kernel(const float* __restri
   }
 }
 
-template <int GW>
+template <int GW, int NW = kW4Waves>
 hipError_t launch_gw(const W4Params& p, int gx, hipStream_t s) {
-  hipLaunchKernelGGL(w4a16_kernel<GW>, dim3(gx, p.S), dim3(kW4Threads), 0, s, p);
+  hipLaunchKernelGGL((w4a16_kernel<GW, NW>), dim3(gx, p.S), dim3(64 * NW), 0, s, p);
   return hipGetLastError();
 }
 
@@ -393,6 +397,14 @@ W4Plan w4a16_plan(int64_t M, int64_t N, int64_t K) {
   int gw = int((gps + kW4Waves - 1) / kW4Waves);
   if (gw == 5 || gw == 7) ++gw;  // slot rings of 3 or 4 need GW in {1, 2, 3, 4, 6, 8}
   pl.gw = gw;
+  pl.nw = kW4Waves;
+  // A split of 7 x 8 groups (K = 28672 in four splits): seven wavefronts of
+  // eight groups each, rather than eight wavefronts of which the last would
+  // hold no group of the split.
+  if (gps == 7 * 8) {
+    pl.gw = 8;
+    pl.nw = 7;
+  }
   pl.ntiles = int(ntiles);
   pl.work_floats = S > 1 ? size_t(S) * size_t(M) * size_t(N) : 0;
   return pl;
@@ -405,7 +417,10 @@ hipError_t launch_w4a16(const W4Params& p0, const W4Plan& pl, int compute_units,
   p.gps = pl.gps;
   p.ntiles = pl.ntiles;
   hipError_t e;
-  switch (pl.gw) {
+  if (pl.nw == 7) {
+    if (pl.gw != 8) return hipErrorInvalidValue;
+    e = launch_gw<8, 7>(p, gx, s);
+  } else switch (pl.gw) {
     case 1: e = launch_gw<1>(p, gx, s); break;
     case 2: e = launch_gw<2>(p, gx, s); break;
     case 3: e = launch_gw<3>(p, gx, s); break;
