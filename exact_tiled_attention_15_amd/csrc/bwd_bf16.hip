@@ -41,6 +41,15 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634074f;
 
+// f(integral_constant<int, I>) for I = B .. E-1, expanded at compile time.
+template <int B, int E, typename F>
+__device__ __attribute__((always_inline)) inline void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 __device__ inline bf16x8 pack8(const float* x) {
   typedef float f32x8 __attribute__((ext_vector_type(8)));
   f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
@@ -364,73 +373,91 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) 
     const char* dotb = qtb + G::T_BYTES;
     const float* l2 = (const float*)(dotb + G::T_BYTES);
     const float* dl = l2 + G::BM;
-    // S and dP of both 32-query blocks: 4 (D/16) MFMA chains, LDS reads run
-    // eight fragments ahead (nothing else on the SIMD covers their latency).
-    f32x16 s[G::QB], dp[G::QB];
+    // The tile's 64 MFMAs, in issue order (h: 32-query block):
+    //   0 .. 31   S[h] and dP[h], h = i / 16, k-slice (i / 2) % 8, S / dP
+    //   32 .. 63  dV^T and dK^T, h = (i - 32) / 16, then half, column block,
+    //             dV / dK
+    // Each needs one A fragment from LDS; the reads run RA MFMAs ahead.  The
+    // P and dS of block 0 are formed between block 1's S / dP products, those
+    // of block 1 between block 0's dV / dK products (16 / (D / 8) elements
+    // per MFMA).
+    // The source order is the schedule.
+    constexpr int NSD = G::QB * (D / 16) * 2;  // S and dP products
+    constexpr int NKV = G::QB * 2 * (D / 32) * 2;  // dV and dK products
+    constexpr int NM = NSD + NKV;
+    constexpr int PER = NSD / G::QB;  // products per block in each phase (D / 8)
+    constexpr int EPS = 16 / PER;     // elements of P / dS per MFMA slot
+    constexpr int RA = 8;
+    static_assert(NKV / G::QB == PER && EPS * PER == 16, "P / dS elements spread evenly over a phase");
+    f32x4 lv[G::QB][4], dv4[G::QB][4];
 #pragma unroll
-    for (int h = 0; h < G::QB; ++h) s[h] = dp[h] = (f32x16){};
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-      for (int h = 0; h < G::QB; ++h) {
-        const bf16x8 a = *(const bf16x8*)(qb + h * 32 * G::KS + r_off + kk * 32);
-        s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[kk], s[h], 0, 0, 0);
-        const bf16x8 b = *(const bf16x8*)(dob + h * 32 * G::KS + r_off + kk * 32);
-        dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, vf[kk], dp[h], 0, 0, 0);
-      }
-    {
-      constexpr int NM = 2 * G::QB * (D / 16);
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-      for (int i = 0; i < NM - 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    }
-#pragma unroll
-    for (int h = 0; h < G::QB; ++h) {
-      // element i: query 32h + 8(i/4) + 4g + i%4 of the tile, key my_k
-      float pr[16], ds[16];
-      f32x4 lv[4], dv4[4];
+    for (int h = 0; h < G::QB; ++h)
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
-        lv[blk] = *(const f32x4*)(l2 + 32 * h + 8 * blk + 4 * g);
-        dv4[blk] = *(const f32x4*)(dl + 32 * h + 8 * blk + 4 * g);
+        lv[h][blk] = *(const f32x4*)(l2 + 32 * h + 8 * blk + 4 * g);
+        dv4[h][blk] = *(const f32x4*)(dl + 32 * h + 8 * blk + 4 * g);
       }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        pr[i] = fast_exp2(fmaf(s[h][i], c, -lv[i / 4][i % 4]));
-        if constexpr (!ALL_LIVE) {
-          const int q = t * G::BM + 32 * h + 8 * (i / 4) + 4 * g + i % 4;
-          if (!(key_ok && q < Nq && (!CAUSAL || my_k <= q + p.diag))) pr[i] = 0.f;
-        }
+    auto frag = [&](int i) {
+      if (i < NSD) {
+        const int h = i / PER, kk = (i / 2) % (D / 16), w = i % 2;
+        return *(const bf16x8*)((w ? dob : qb) + h * 32 * G::KS + r_off + kk * 32);
       }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) ds[i] = pr[i] * (dp[h][i] - dv4[i / 4][i % 4]);
-      const bf16x8 pp[2] = {pack8(pr), pack8(pr + 8)};
-      const bf16x8 pd[2] = {pack8(ds), pack8(ds + 8)};
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int off = db * 32 * G::VTP + t_off + (32 * h + 16 * half) * 2;
-          const bf16x8 a = *(const bf16x8*)(dotb + off);
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pp[half], dv[db], 0, 0, 0);
-          const bf16x8 b = *(const bf16x8*)(qtb + off);
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, pd[half], dk[db], 0, 0, 0);
-        }
-      {
-        constexpr int NM = 2 * 2 * (D / 32);
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-        for (int i = 0; i < NM - 8; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      const int j = i - NSD, h = j / PER, half = (j / 2) / (D / 32) % 2, db = (j / 2) % (D / 32), w = j % 2;
+      const int off = db * 32 * G::VTP + t_off + (32 * h + 16 * half) * 2;
+      return *(const bf16x8*)((w ? qtb : dotb) + off);
+    };
+    f32x16 s[G::QB], dp[G::QB];
+    float pr[16], ds[16];
+    bf16x8 pp[G::QB][2], pd[G::QB][2];
+    // element e of block h: query 32h + 8(e/4) + 4g + e%4 of the tile, key my_k
+    auto elem = [&](int h, int e) {
+      float v = fast_exp2(fmaf(s[h][e], c, -lv[h][e / 4][e % 4]));
+      if constexpr (!ALL_LIVE) {
+        const int q = t * G::BM + 32 * h + 8 * (e / 4) + 4 * g + e % 4;
+        if (!(key_ok && q < Nq && (!CAUSAL || my_k <= q + p.diag))) v = 0.f;
       }
-    }
+      pr[e] = v;
+      ds[e] = v * (dp[h][e] - dv4[h][e / 4][e % 4]);
+      if (e == 7) {
+        pp[h][0] = pack8(pr);
+        pd[h][0] = pack8(ds);
+      } else if (e == 15) {
+        pp[h][1] = pack8(pr + 8);
+        pd[h][1] = pack8(ds + 8);
+      }
+    };
+    bf16x8 fa[RA];
+#pragma unroll
+    for (int i = 0; i < RA; ++i) fa[i] = frag(i);
+    // Unrolled at compile time (every array index below is a constant).
+    static_for<0, NM>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      const bf16x8 a = fa[i % RA];
+      if (i < NSD) {
+        const int h = i / PER, kk = (i / 2) % (D / 16);
+        if (i % 2 == 0)
+          s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[kk], kk == 0 ? (f32x16){} : s[h], 0, 0, 0);
+        else
+          dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[kk], kk == 0 ? (f32x16){} : dp[h], 0, 0, 0);
+      } else {
+        const int j = i - NSD, h = j / PER, half = (j / 2) / (D / 32) % 2, db = (j / 2) % (D / 32);
+        if (j % 2 == 0)
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pp[h][half], dv[db], 0, 0, 0);
+        else
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pd[h][half], dk[db], 0, 0, 0);
+      }
+      if (i + RA < NM) fa[i % RA] = frag(i + RA);
+      // P / dS of block 0 during block 1's S / dP, of block 1 during block 0's dV / dK
+#pragma unroll
+      for (int u = 0; u < EPS; ++u) {
+        if (i >= PER && i < 2 * PER) elem(0, (i - PER) * EPS + u);
+        if (i >= NSD && i < NSD + PER) elem(1, (i - NSD) * EPS + u);
+      }
+      // Keep this order: with one wavefront per SIMD nothing else hides the
+      // LDS latency, and the scheduler would otherwise sink the reads to
+      // their MFMAs to save registers.
+      __builtin_amdgcn_sched_barrier(0);
+    });
     if (more) lstore(t + 1);
     __syncthreads();
   };
