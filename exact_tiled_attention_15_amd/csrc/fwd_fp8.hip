@@ -357,26 +357,41 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
   auto qk = [&](const char* kb, f32x16 (&s)[G::KB]) {
 #pragma unroll
     for (int h = 0; h < G::KB; ++h) s[h] = (f32x16){};
+    // Fragment i = (k-slice i / KB, block i % KB); the LDS reads run RA
+    // fragments ahead of the MFMAs, in source order, pinned (left to itself
+    // the scheduler reads each fragment right before its MFMA).
     if constexpr (QK16) {
+      constexpr int NF = G::KB * (D / 16), RA = 4;
+      auto frag = [&](int i) { return *(const f16x8*)(kb + k_off + (i % G::KB) * 32 * G::KS + (i / G::KB) * 32); };
+      f16x8 fa[RA];
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
+      for (int i = 0; i < RA; ++i) fa[i] = frag(i);
 #pragma unroll
-        for (int h = 0; h < G::KB; ++h) {
-          const f16x8 a = *(const f16x8*)(kb + k_off + h * 32 * G::KS + kk * 32);
-          s[h] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf16[kk], s[h], 0, 0, 0);
-        }
+      for (int i = 0; i < NF; ++i) {
+        const int kk = i / G::KB, h = i % G::KB;
+        s[h] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i % RA], qf16[kk], kk == 0 ? (f32x16){} : s[h], 0, 0, 0);
+        if (i + RA < NF) fa[i % RA] = frag(i + RA);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     } else {
+      constexpr int NF = G::KB * (D / 64), RA = 2;
+      auto frag = [&](int i) {
+        const char* ap = kb + k_off + (i % G::KB) * 32 * G::KS + (i / G::KB) * 64;
+        const u32x4 a0 = *(const u32x4*)ap;
+        const u32x4 a1 = *(const u32x4*)(ap + 16);
+        return (i32x8){(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+      };
+      i32x8 fa[RA];
 #pragma unroll
-      for (int kk = 0; kk < D / 64; ++kk)
+      for (int i = 0; i < RA; ++i) fa[i] = frag(i);
 #pragma unroll
-        for (int h = 0; h < G::KB; ++h) {
-          const char* ap = kb + k_off + h * 32 * G::KS + kk * 64;
-          const u32x4 a0 = *(const u32x4*)ap;
-          const u32x4 a1 = *(const u32x4*)(ap + 16);
-          const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                           (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-          s[h] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf8[kk], s[h], 0, 0, 0, 127, 0, 127);
-        }
+      for (int i = 0; i < NF; ++i) {
+        const int kk = i / G::KB, h = i % G::KB;
+        s[h] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i % RA], qf8[kk], kk == 0 ? (f32x16){} : s[h], 0, 0,
+                                                               0, 127, 0, 127);
+        if (i + RA < NF) fa[i % RA] = frag(i + RA);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
   auto mask = [&](f32x16 (&s)[G::KB], int k0) {
@@ -418,16 +433,31 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
     }
   }
 
+  // The K and V scales of a tile are fetched one tile ahead with vector
+  // loads (the offset is opaque to the compiler, so it cannot turn them into
+  // scalar loads): an outstanding scalar load shares the LDS wait counter and
+  // would make every LDS wait of the tile a full drain.
+  auto scale_pair = [&](int t, float& ks, float& vs) {
+    int z = 0;
+    asm volatile("" : "+v"(z));
+    const int i = (t * BN) / QT + z;
+    ks = ksc[i];
+    vs = vsc[i];
+  };
+  float ks_next = 0.f, vs_next = 0.f;
+  if (ntiles > 0) scale_pair(0, ks_next, vs_next);
   for (int t = 0; t < ntiles; ++t) {
     const bool more = t + 1 < ntiles;
+    const float ks_t = ks_next, vs_t = vs_next;
     if (more) {
       load_k(t + 1);
       gload_v(t + 1);
+      scale_pair(t + 1, ks_next, vs_next);
     }
     if (t < wtiles) {
       const int k0 = t * BN;
-      const float c = c_q * ksc[k0 / QT];
-      const float sv = vsc[k0 / QT];
+      const float c = c_q * ks_t;
+      const float sv = vs_t;
       const float vfold = __log2f(sv * inv_svmax);  // <= 0
       const float vunfold = svmax / sv;
 
