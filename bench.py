@@ -43,10 +43,21 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 
 # rocprofv3 FETCH_SIZE/WRITE_SIZE summaries (copy-calibrated) per workload; the
 # figure is reported only while the kernel sources still hash to the value the
-# counters were taken with.
+# counters were taken with.  Bytes per step: all kernel launches of one step.
 TRAFFIC_PROFILES = {
-    "bf16_causal_B8_H16_N2048_d128": "profiles/fwd_bf16_causal_B8_H16_N2048_d128_hbm_traffic.txt",
-    "w4a16_decode_M16_N28672_K8192_G128": "profiles/w4a16_decode_M16_N28672_K8192_G128_hbm_traffic.txt",
+    w: f"profiles/{w}_hbm_traffic.txt"
+    for w in (
+        "bf16_causal_B8_H16_N2048_d128",
+        "bf16_causal_B1_H8_N32768_d128",
+        "bf16_kvblocks_B1_H16_Nq8192_Nk65536x8_d128",
+        "bf16_causal_ring_B1_H16_N65536_R8_d128",
+        "fp8_B4_H16_N4096_d128",
+        "fp8_norot_qk16_B4_H16_N4096_d128",
+        "bwd_bf16_causal_B8_H16_N2048_d128",
+        "f32_B1_H2_N256_d64",
+        "w4a16_decode_M16_N28672_K8192_G128",
+        "w4a16_decode_M16_N8192_K28672_G128",
+    )
 }
 
 
@@ -69,7 +80,7 @@ def measured_traffic(workload):
                 h.update(f.read())
         if h.hexdigest() != fields["kernel_source_sha256"]:
             return None
-        return int(fields["traffic_bytes_per_launch"])
+        return int(fields["traffic_bytes_per_step"])
     except (KeyError, OSError, ValueError):
         return None
 
@@ -370,7 +381,7 @@ def main():
         "unit": "TFLOP/s",
         "frac": round(tflops / peak, 4),
         "traffic": measured_traffic(name),
-        "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+        "traffic_unit": "bytes per step, all launches (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
         "launches_per_step": launches,
     }
 
@@ -567,7 +578,7 @@ def bench_w4a16(args, name, cfg):
         "unit": "GB/s",
         "frac": round(gbs / PEAK_HBM_GBS, 4),
         "traffic": measured_traffic(name),
-        "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+        "traffic_unit": "bytes per step, all launches (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
         "algorithmic_bytes": nbytes,
         "launches_per_step": 2 if nw else 1,
     }
