@@ -41,14 +41,6 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634074f;
 
-// f(integral_constant<int, I>) for I = B .. E-1, expanded at compile time.
-template <int B, int E, typename F>
-__device__ __attribute__((always_inline)) inline void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
 
 __device__ inline bf16x8 pack8(const float* x) {
   typedef float f32x8 __attribute__((ext_vector_type(8)));

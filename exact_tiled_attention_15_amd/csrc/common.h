@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 namespace eta {
 
@@ -191,6 +192,15 @@ __device__ inline float halves_sum(float x) {
 }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// f(integral_constant<int, I>) for I = B .. E-1, expanded at compile time.
+template <int B, int E, typename F>
+__device__ __attribute__((always_inline)) inline void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // One wave-wide direct load of 64 x 16 bytes from global memory into LDS at
 // lds_base + 16 * lane.  Issued as assembly so the compiler does not treat
