@@ -19,8 +19,10 @@
 //     the softmax FMA: c_t = |scale| * log2(e) * s_q * s_k(t).
 //   * P V on the 32x32x16 fp16 MFMA: V codes are converted exactly to fp16
 //     while staged into LDS; the probabilities are rounded to fp16 as
-//     p * s_v(t) / max_t s_v (the ratio folded into the exponent bias, so the
-//     value is <= 1 for any scales), and the normaliser is summed from the
+//     p * s_v(t) / max_t s_v (the ratio folded into the exponent bias), with
+//     p taken against a reference maximum that moves only when the row's
+//     maximum passes it by more than 2^8, so the value is <= 2^8 for any
+//     scales and O is rarely rescaled; the normaliser is summed from the
 //     unrounded fp32 values with the ratio divided out once per tile.
 //   * PV8 instantiation (the FlashAttention-3 FP8 form of the same passage,
 //     probabilities in fp8 too): P V on the 32x32x64 f8f6f4 MFMA with V's
@@ -55,6 +57,9 @@
 namespace eta {
 
 constexpr int kQuantTile = 128;  // tokens per quantization tile
+// fp16 probabilities are taken against a reference maximum that moves only
+// when a row's maximum passes it by more than this many powers of two.
+constexpr float kLazyLog2 = 8.f;
 
 // How P.V runs: fp16 P against fp16-widened V codes, or P in e4m3 / e2m1
 // against V's e4m3 codes on the f8f6f4 MFMA (e2m1 by rounding the exponential,
@@ -195,7 +200,8 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
   // this wavefront's query scale tile (its 32 rows never straddle two)
   const float c_q = p.c * p.q_scale[(int64_t)bh * nqt + min(qw0, Nq - 1) / QT];
   // Largest V scale of this (b,h) slice: probabilities are stored as
-  // p * s_v(t) / svmax <= 1, which fp16 holds without overflow.
+  // p * s_v(t) / svmax, at most 2^8 in fp16 (2^8 in e4m3, 4 in e2m1 after
+  // their fixed factors), which holds without overflow.
   float svmax = 0.f;
   for (int t = 0; t < nkt; ++t) svmax = fmaxf(svmax, vsc[t]);
   const float inv_svmax = 1.f / svmax;
@@ -348,7 +354,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = (f32x16){};
-  float m2 = -INFINITY;  // running max of c_t * raw, base-2 units
+  float m2 = -INFINITY;  // reference maximum of c_t * raw, base-2 units
   float l_lane = 0.f;
 
   const int k_off = r32 * G::KS + g * (QK16 ? 16 : 32);
@@ -394,15 +400,16 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
       }
     }
   };
+  // Element i of block h holds key k0 + 32 h + 4 g + 8 (i / 4) + i % 4: the
+  // test is against a per-lane limit and a constant offset.
   auto mask = [&](f32x16 (&s)[G::KB], int k0) {
     const int lim = CAUSAL ? min(my_q + p.diag, Nk - 1) : Nk - 1;
+    const int dl = lim - k0 - 4 * g;
 #pragma unroll
     for (int h = 0; h < G::KB; ++h)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = k0 + 32 * h + 8 * (i >> 2) + 4 * g + (i & 3);
-        if (key > lim) s[h][i] = -INFINITY;
-      }
+      for (int i = 0; i < 16; ++i)
+        if (32 * h + 8 * (i >> 2) + (i & 3) > dl) s[h][i] = -INFINITY;
   };
 
   if (ntiles > 0) {
@@ -459,7 +466,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
       const float c = c_q * ks_t;
       const float sv = vs_t;
       const float vfold = __log2f(sv * inv_svmax);  // <= 0
-      const float vunfold = svmax / sv;
+      const float vunfold = svmax * __builtin_amdgcn_rcpf(sv);
 
       f32x16 s[G::KB];
       qk(kstage(t), s);
@@ -472,7 +479,12 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[h][i]);
       mx = halves_max(mx);
       const float mx2 = mx == -INFINITY ? -INFINITY : mx * c;
-      const bool need = mx2 > m2;
+      // fp16 probabilities: the reference moves only when the maximum passes
+      // it by more than kLazyLog2 (P' then stays below 2^8, which fp16 holds
+      // with its full 11-bit precision), so O and l are rarely rescaled.  The
+      // fp8 and fp4 probabilities keep the exact maximum (their scaled range
+      // is fixed).
+      const bool need = mx2 > m2 + (PV8 ? 0.f : kLazyLog2);
       if (__ballot(need)) {
         const float m_new = need ? mx2 : m2;
         const float alpha = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - m_new);
