@@ -303,16 +303,15 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
   // Keys beyond the causal limit or the end of K; exp2(-inf * c) = 0 as c > 0.
-  // Element i of block h holds key k0 + 32 h + 4 g + 8 (i / 4) + i % 4: the
-  // test is against a per-lane limit and a constant offset.
   auto mask = [&](f32x16 (&s)[G::KB], int k0, int my_q) {
     const int lim = CAUSAL ? min(my_q + p.diag, Nk - 1) : Nk - 1;
-    const int dl = lim - k0 - 4 * g;
 #pragma unroll
     for (int h = 0; h < G::KB; ++h)
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (32 * h + 8 * (i >> 2) + (i & 3) > dl) s[h][i] = -INFINITY;
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + 32 * h + 8 * (i >> 2) + 4 * g + (i & 3);
+        if (key > lim) s[h][i] = -INFINITY;
+      }
   };
   auto rowmax = [&](const f32x16 (&s)[G::KB]) {
     float mx = s[0][0];
