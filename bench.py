@@ -7,9 +7,11 @@ One step = one pass of the hot path over one batch of synthetic input:
 W untimed warm-up steps, then K steps back to back on one stream, bracketed
 by HIP events recorded on that stream (torch.cuda.Event on the stream the
 kernels are launched on) and device synchronisation.  The warm-up runs at
-least --warmup steps (default 10) and at least 0.3 s: an idle MI355X needs
-about 0.1-0.2 s of load to leave its low clocks, and a 5-step warm-up of the
-causal B8 H16 N2048 workload (1 ms) measures ~665 instead of ~840 TFLOP/s.
+least --warmup steps (default 10) and at least 2 s: an idle MI355X needs
+about 0.1-0.2 s of load to leave its low clocks (a 5-step warm-up of the
+causal B8 H16 N2048 workload, 1 ms, measures ~665 instead of ~840 TFLOP/s),
+and two seconds of GPU work also make the run visible to a utilisation
+sampler next to the CPU baseline's second of host work.
 The JSON line's "warmup" is the requested minimum; "warmup_steps_run" and
 "warmup_s" are what actually ran.  Inputs are
 resident in HBM before the timed region starts.  Prints one JSON line.
@@ -102,7 +104,7 @@ def parse():
     return ap.parse_args()
 
 
-WARMUP_SECONDS = 0.3
+WARMUP_SECONDS = 2.0
 
 
 def warm_up(step, warmup):

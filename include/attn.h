@@ -22,7 +22,8 @@
  *    on the host, enqueues its kernels on `stream` (a hipStream_t; NULL means
  *    the default stream) and returns.  Global state is limited to two caches
  *    that live until the process ends and never change a result: each device's
- *    compute-unit count (read once, used to size the W4A16 grid), and
+ *    compute-unit count (read once, used to size the W4A16 grid and the bf16
+ *    forward's persistent grid), and
  *    attn_fwd_ring_host's per-device copy stream with five events, created on
  *    that entry point's first call on the device and guarded by a mutex.
  *  - Layout: contiguous [B, H, N, d] row-major, d innermost; per-row outputs
@@ -78,13 +79,15 @@ const char* attn_status_str(attn_status s);
  *   o   bf16 [B,H,Nq,d]     O = P V with P = softmax of the allowed scores,
  *                           accumulated in fp32, rounded to nearest-even once.
  *   lse fp32 [B,H,Nq]       may be NULL (not written).
- * The outer loop runs over 256-row query blocks (one workgroup of 8
- * wavefronts each, spread over all compute units: sequence-length
- * parallelism); the inner loop streams 128-key K/V tiles through LDS (double
- * buffered), keeps the running max / normaliser per row and divides by the
- * normaliser once after the loop ("FlashAttention-2", Systems analysis wiki,
- * "Technical architecture and working principles", items 1-3).  Causal key
- * tiles above the diagonal are skipped wholesale.
+ * The outer loop runs over 256-row query blocks, spread over all compute
+ * units (sequence-length parallelism): one persistent workgroup of 8
+ * wavefronts per compute unit walks its share of the blocks, longest first;
+ * the inner loop streams 128-key K/V tiles through LDS (double buffered, the
+ * stream running on across block boundaries), keeps the running max /
+ * normaliser per row and divides by the normaliser once after the loop
+ * ("FlashAttention-2", Systems analysis wiki, "Technical architecture and
+ * working principles", items 1-3).  Causal key tiles above the diagonal are
+ * skipped wholesale.
  */
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int H, int Nq, int Nk, int d, int causal, float scale,
