@@ -17,8 +17,8 @@
 // Computing S^T (rows = keys, columns = queries) leaves each lane with one
 // query's scores for 16 keys of a 32-key block, so row max / sum are in-lane
 // plus one permlane32 swap, and the scores feed O^T = V^T P^T as the B
-// operand without any data movement.  The V^T fragments are single 16-byte
-// LDS reads from the transposed, key-permuted V tile (common.h).
+// operand without any data movement.  The V^T fragments come from the
+// row-major V tile by two transposing LDS reads (ds_read_b64_tr_b16) each.
 //
 // Issue order.  The probabilities of each 32-key block are formed right
 // before that block's P.V products, so the exponentials of the next block
@@ -28,9 +28,10 @@
 //
 // Staging.  A workgroup of W wavefronts owns 32*W query rows (W = 8: one
 // workgroup per compute unit, two wavefronts per SIMD), so every K/V tile read
-// from memory serves 256 rows.  K tiles go straight from global memory into LDS
-// (global_load_lds); V goes through registers so it can be stored transposed.
-// Tile t+1 is in flight while tile t is computed; one barrier per tile.
+// from memory serves 256 rows.  K and V tiles go straight from global memory
+// into LDS (buffer loads with an LDS destination), with no registers and no
+// vector work on the way.  Tile t+1 is in flight while tile t is computed; one
+// barrier per tile.
 //
 // Rescaling.  O and l are multiplied by alpha only on tiles where some row of
 // the wavefront raised its maximum (one ballot per tile).  The exponent always
@@ -45,22 +46,18 @@ struct Geo {
   static constexpr int THREADS = 64 * W;
   static constexpr int BM = 32 * W;           // query rows per workgroup
   static constexpr int KB = BN / 32;          // 32-key blocks per tile
-  static constexpr int VTP = vt_pitch(BN);    // V^T row pitch (bytes)
-  static constexpr int KS = D * 2;            // K tile row pitch (bytes): unpadded, chunks permuted
+  static constexpr int KS = D * 2;            // K / V tile row pitch (bytes): unpadded, permuted
   static constexpr int K_BYTES = BN * KS;
-  static constexpr int V_BYTES = D * VTP;     // V^T: one row per column d
+  static constexpr int V_BYTES = BN * KS;
   static constexpr int LDS = 2 * K_BYTES + 2 * V_BYTES;  // two K stages, two V stages
   static constexpr int CPR = D / 8;           // 16-byte chunks per row (K, Q and O blocks)
   static constexpr int RPT = 64 / CPR;        // rows per wave-wide 1 KiB transfer
   static constexpr int K_LOADS = BN / RPT;    // transfers per K tile
   static constexpr int KPW = K_LOADS / W;     // ... per wavefront
-  static constexpr int KG = BN / 4;           // 4-key groups per tile
-  static constexpr int V_THREADS = KG * (D / 8);  // key groups x D/8 column chunks
   static_assert(KPW * W == K_LOADS, "K tile must be whole transfers per wavefront");
   // Wavefront w issues transfers w + W n: the chunk permutation of a row
   // (row mod CPR) is then the same for all of one lane's transfers.
   static_assert((RPT * W) % CPR == 0 && 32 % CPR == 0, "row permutation constant per lane");
-  static_assert(V_THREADS <= THREADS, "V staging needs at most one thread per 4x8 block");
   // The bf16 O block of the epilogue (rows of 2D bytes, chunks permuted) goes
   // half into a stage's K tile and half into its V tile.
   static_assert((BM / 2) * 2 * D <= K_BYTES && (BM / 2) * 2 * D <= V_BYTES, "O and Q halves fit a stage");
@@ -134,9 +131,10 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
   // (row mod CPR) of row l / CPR into slot l mod CPR, which is one constant
   // offset per lane for all of its transfers.  The buffer's range ends at the
   // last key, so rows past Nk read as zero (or keep older data): such keys are
-  // always masked.  V: through registers, thread (dc, kgrp) takes keys
-  // 4*kgrp .. +3 of columns 8*dc .. +7 and stores them transposed (common.h).
-  u32x4 vreg[4];
+  // always masked.  V: the same transfers, rows kept whole but their 64-byte
+  // segments (32 columns) permuted: segment c of key row r sits at c ^ f(r),
+  // f(r) = r mod 4 (d = 128) or (r ^ r / 2) mod 2 (d = 64), so that the
+  // transposing fragment reads of the P.V products below hit distinct banks.
   auto kstage = [&](int s) { return smem + s * G::K_BYTES; };
   auto vstage = [&](int s) { return smem + 2 * G::K_BYTES + s * G::V_BYTES; };
   // LDS byte addresses of the stages for the transfers, from the array itself
@@ -151,6 +149,13 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
     return (unsigned)(row * 2 * D + 16 * ((l % G::CPR) ^ (row & (G::CPR - 1))));
   };
   const unsigned k_lane = chunk_lane(lane);
+  // V: lane l loads row RPT * wave + l / CPR, the 16-byte chunk whose
+  // segment lands in its slot l mod CPR after the permutation.
+  auto vseg = [](int r) { return D == 128 ? (r & 3) : ((r ^ (r >> 1)) & 1); };
+  const unsigned v_lane = [&]() {
+    const int l = lane, row = G::RPT * wave + l / G::CPR, jc = l % G::CPR;
+    return (unsigned)(row * 2 * D + 16 * (4 * ((jc >> 2) ^ vseg(row)) + (jc & 3)));
+  }();
   auto load_k = [&](int bh, int t, int s) {
     const int k0 = t * BN;
     const i32x4 rsrc = buffer_rsrc_n((const uint16_t*)p.k + ((int64_t)bh * Nk + k0) * D,
@@ -163,22 +168,18 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
     for (int n = 0; n < G::KPW; ++n)
       buf_lds16<0, 1024 * W>(rsrc, k_lane + (unsigned)(n * G::RPT * W * 2 * D), soff, lds);
   };
-  // V rows past Nk read as zero through the buffer's range: their
-  // probabilities are exactly 0, and 0 * 0 adds nothing.
-  auto gload_v = [&](int bh, int t) {
-    const int ft = wave * 64 + fresh_lane();
-    if (ft >= G::V_THREADS) return;
+  // V rows past Nk read as zero (or keep older data) through the buffer's
+  // range: their probabilities are exactly 0, and 0 times any finite value
+  // adds nothing.
+  auto load_v = [&](int bh, int t, int s) {
     const int k0 = t * BN;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const uint16_t*)p.v + ((int64_t)bh * Nk + k0) * D), (short)0, min(BN, Nk - k0) * 2 * D,
-        0x00020000);
-    const int off = (4 * (ft % G::KG)) * 2 * D + 16 * (ft / G::KG);
+    const i32x4 rsrc = buffer_rsrc_n((const uint16_t*)p.v + ((int64_t)bh * Nk + k0) * D,
+                                     (unsigned)(min(BN, Nk - k0) * 2 * D));
+    unsigned soff = 0;
+    unsigned lds = __builtin_amdgcn_readfirstlane(vstage_lds(s) + 1024u * wave);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) vreg[r] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + r * 2 * D, 0, 0);
-  };
-  auto lstore_v = [&](int s) {
-    const int ft = wave * 64 + fresh_lane();
-    if (ft < G::V_THREADS) store_vt(vstage(s), G::VTP, 8 * (ft / G::KG), ft % G::KG, vreg);
+    for (int n = 0; n < G::KPW; ++n)
+      buf_lds16<0, 1024 * W>(rsrc, v_lane + (unsigned)(n * G::RPT * W * 2 * D), soff, lds);
   };
   // Direct loads are counted by vmcnt only: drain them before the barrier that
   // publishes the stage.
@@ -274,7 +275,18 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
   // at slot (2kk + g) ^ (r32 mod CPR) = 2kk ^ (g ^ (r32 mod CPR)).
   const int k_off = r32 * G::KS;
   const int k_x = 16 * (g ^ (r32 & (G::CPR - 1)));
-  const int v_off = r32 * G::VTP + g * 16;   // V^T row r32 of a 32-column block, slot 8g
+  // V^T fragment of block h, half, column block db (A operand: row d = 32 db
+  // + l % 32, k = keys 8g .. 8g+7 of the half in P's key order, which is
+  // 4g .. 4g+3 and 8+4g .. 8+4g+3): two transposing reads of 8-byte row pieces.
+  // Within each 16-lane group, lane i receives element i % 4 of the pieces
+  // addressed by lanes i / 4 + 4j (j = 0..3), so lane (q = (l / 16) % 2, m =
+  // (l % 16) / 4, e = l % 4) addresses key 4g + m, columns 16 q + 4 e of the
+  // segment: lane l then holds column 32 db + l % 32 of keys 4g .. 4g+3; the
+  // second read (8 keys on) the other four.
+  const unsigned v_frag = [&]() {
+    const int vq = (lane >> 4) & 1, vm = (lane & 15) >> 2, ve = lane & 3;
+    return (unsigned)((4 * g + vm) * 2 * D + 64 * vseg(4 * g + vm) + 32 * vq + 8 * ve);
+  }();
 
   // S^T = K Q^T for one tile: fragment i = (kk, h) = (i / KB, i % KB).  The
   // source order is already the schedule (LDS reads four fragments ahead of
@@ -339,7 +351,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
   // exponentials of block h+1 issue between them, and the V^T fragments are
   // read four MFMAs ahead.  The source order is that schedule (the scheduling
   // groups below ask for the same).  The row sum runs in four partial sums.
-  auto softmax_pv = [&](const f32x16 (&s)[G::KB], const char* vb) {
+  auto softmax_pv = [&](const f32x16 (&s)[G::KB], unsigned vb) {
     const float bias = (m_run == -INFINITY) ? 0.f : -m_run * c;
     float rs[4] = {0.f, 0.f, 0.f, 0.f};
     constexpr int MPB = 2 * (D / 32);  // MFMAs per 32-key block
@@ -347,7 +359,10 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
     constexpr int EPM = 16 / MPB;      // next block's exponentials per MFMA
     auto vfrag = [&](int i) {
       const int h = i / MPB, db = (i % MPB) / 2, half = i % 2;
-      return *(const bf16x8*)(vb + v_off + db * 32 * G::VTP + (32 * h + 16 * half) * 2);
+      const unsigned a = ((vb + v_frag) ^ (unsigned)(64 * db)) + (unsigned)((32 * h + 16 * half) * 2 * D);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(a + 16 * D));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     auto probs = [&](int h, int j0, float* pv) {
 #pragma unroll
@@ -385,11 +400,11 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
     constexpr int VPB = 56;                   // vector instructions per block's probabilities
     constexpr int VPM = (VPB + MPB - 1) / MPB;  // per MFMA: one block's worth per block's MFMAs
     __builtin_amdgcn_sched_group_barrier(0x002, VPB, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // two transposing reads per fragment
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i + 4 < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i + 4 < NM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
     }
   };
@@ -518,10 +533,9 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
     if (!have_t0 || !have_q) {
       if (!have_t0 && cur.ntiles > 0) {
         load_k(cur.bh, 0, st);
-        gload_v(cur.bh, 0);
+        load_v(cur.bh, 0, st);
       }
       if (!have_q) load_q_lds(cur, st ^ 1);
-      if (!have_t0 && cur.ntiles > 0) lstore_v(st);
       publish();
       if (!have_q) {
         read_q_lds(st ^ 1);
@@ -543,7 +557,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
       const int lt = last ? 0 : t + 1;
       if (fill) {
         load_k(lbh, lt, st ^ 1);
-        gload_v(lbh, lt);
+        load_v(lbh, lt, st ^ 1);
       }
       f32x16 sc[G::KB];
       if (t < cur.wtiles) {
@@ -556,8 +570,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
         load_q_regs(nxt);  // the fragments are free once the products above are issued
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (t < cur.wtiles) softmax_pv(sc, vstage(st));
-      if (fill) lstore_v(st ^ 1);
+      if (t < cur.wtiles) softmax_pv(sc, vstage_lds(st));
       publish();
       st ^= 1;
     }
