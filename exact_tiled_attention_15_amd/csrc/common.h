@@ -108,6 +108,31 @@ __device__ inline int sched_block(int k, int w, int G, int n) {
   return r < n ? r : -1;
 }
 
+// Causal persistent schedule in pairs.  Query block j of a slice sees j + 1
+// diagonal-aligned key ranges of the block size and block nqb-1-j sees nqb - j,
+// so the pair (nqb-1-j, j) always carries nqb + 1 of them: a workgroup that
+// takes whole pairs gets an exact share of the tiles.  Workgroup w (XCD
+// w % 8) takes units u = r * G/8 + w / 8, r = 0, 1, ..., of its XCD's
+// (BH/8) * (nqb/2) units; unit u is pair u % (nqb/2) of the XCD's slice
+// u / (nqb/2), heavier block first.  The workgroups of an XCD that run at the
+// same time therefore cover few slices, and the ones on the same slice stream
+// its K/V tiles in step, out of the XCD's L2.  Returns the k-th block of
+// workgroup w in map_block's numbering, or -1 when there is none.  Used when
+// every workgroup gets at least one pair (fewer pairs than workgroups would
+// leave some idle that the per-block schedule keeps busy).
+__device__ inline bool pair_sched_ok(int G, int nqb, int BH) {
+  return (G & 7) == 0 && (BH & 7) == 0 && (nqb & 1) == 0 && (BH >> 3) * (nqb >> 1) >= (G >> 3);
+}
+__device__ inline int sched_block_pairs(int k, int w, int G, int nqb, int BH) {
+  const int x = w & 7, i = w >> 3, gx = G >> 3;
+  const int hp = BH >> 3, np = nqb >> 1;
+  const int u = (k >> 1) * gx + i;
+  if (u >= hp * np) return -1;
+  const int s = u / np, j = u % np;
+  const int qi = (k & 1) ? nqb - 1 - j : j;  // map_block turns qi into qb = nqb - 1 - qi
+  return 8 * (qi * hp + s) + x;
+}
+
 // Launchers (host side). Each returns hipGetLastError() after the launch.
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, int epi, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t s);

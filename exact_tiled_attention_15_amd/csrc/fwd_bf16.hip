@@ -93,14 +93,17 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
   };
 
   // ---- the blocks of this workgroup.  A block is (b*h slice, 256-row query
-  // block); the workgroup walks its blocks in sched_block order.  Per block:
+  // block); the workgroup walks its blocks in sched_block_pairs order (causal,
+  // when the grid allows it) or sched_block order.  Per block:
   // the key range of the workgroup (tiles at or beyond it are skipped
   // wholesale) and of this wavefront.
   struct Blk {
     int q0, bh, ntiles, wtiles, wmask_from;
   };
   auto describe = [&](int k, Blk& b) {
-    const int gi = sched_block(k, blockIdx.x, gridDim.x, nblocks);
+    const int gi = (CAUSAL && pair_sched_ok(gridDim.x, p.nqb, p.BH))
+                       ? sched_block_pairs(k, blockIdx.x, gridDim.x, p.nqb, p.BH)
+                       : sched_block(k, blockIdx.x, gridDim.x, nblocks);
     if (gi < 0) return false;
     int qb, bh;
     map_block(block_perm(p, gi, nblocks), p.nqb, p.BH, CAUSAL, qb, bh);

@@ -63,10 +63,11 @@ def test_attn_fwd_small_shapes(B, H, Nq, Nk, d, causal):
 # and Q rows loading during the previous block's last tile.  Ragged last
 # blocks, blocks with no allowed key (causal, Nq - Nk >= 256: rows with no key
 # get O = 0 and LSE = -inf), d = 64, and block counts that are and are not
-# multiples of 8 (per-XCD and plain schedules).
+# multiples of 8 (per-XCD and plain schedules).  The last case is causal with
+# a pair of query blocks for every workgroup (the paired causal schedule).
 SEVERAL_BLOCKS = [
     (1, 160, 300, 300, 128, True), (1, 100, 600, 40, 128, True), (2, 65, 257, 257, 64, False),
-    (1, 264, 256, 129, 128, True), (3, 97, 512, 300, 128, False),
+    (1, 264, 256, 129, 128, True), (3, 97, 512, 300, 128, False), (4, 64, 512, 512, 64, True),
 ]
 
 
