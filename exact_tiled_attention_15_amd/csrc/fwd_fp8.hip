@@ -165,6 +165,17 @@ __device__ inline void store_vt8(char* vt, int pitch, int d0, int kg, const u32x
   }
 }
 
+// Non-causal grids of one workgroup per block: block g runs on XCD g % 8 (the
+// dispatcher's round robin) and the workgroups an XCD holds at a time are
+// consecutive in g / 8, so taking the query blocks of one slice in a row
+// (slice-major) keeps few slices' K/V in that XCD's L2 at once.  Every block
+// has the same length, so the order costs no balance.  BH a multiple of 8.
+__device__ inline void map_block_slices(int g, int nqb, int BH, int& qb, int& bh) {
+  const int x = g & 7, t = g >> 3, hp = BH >> 3;
+  bh = x * hp + t / nqb;
+  qb = t % nqb;
+}
+
 template <int D, bool CAUSAL, bool QK16, int PVM, int W, int BN>
 __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
   constexpr bool PV8 = PVM != kPvF16;  // P.V on the f8f6f4 MFMA with V's codes
@@ -185,7 +196,10 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
   const int g = lane >> 5;
 
   int qb, bh;
-  map_block(tile_index(p), p.nqb, p.BH, CAUSAL, qb, bh);
+  if (!CAUSAL && (p.BH & 7) == 0)
+    map_block_slices(tile_index(p), p.nqb, p.BH, qb, bh);
+  else
+    map_block(tile_index(p), p.nqb, p.BH, CAUSAL, qb, bh);
   const int q0 = qb * G::BM;
   const int qw0 = q0 + wave * 32;
   const int my_q = qw0 + r32;
