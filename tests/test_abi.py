@@ -231,3 +231,26 @@ def test_mfma_probe_validation_and_flop():
     assert eta.mfma_peak_flop(eta.MFMA_FP8, 3, 5) == 3 * 8 * 5 * 4 * 2 * 32 * 32 * 64
     assert eta.mfma_peak_flop(eta.MFMA_F32, 1, 1) == 8 * 4 * 2 * 32 * 32 * 2
     assert eta.mfma_peak_flop(9, 1, 1) == 0 and eta.mfma_peak_flop(eta.MFMA_BF16, 0, 1) == 0
+
+
+# Entry points that allocate device (or pinned host) memory.  The library's
+# calls work in caller-owned buffers (the pages' O(N)-memory property: no N x N
+# matrix, and here no allocation at all), so its dynamic symbol table must not
+# import any of them.
+ALLOCATORS = ("hipMalloc", "hipExtMalloc", "hipHostMalloc", "hipHostAlloc", "hipFree", "hipMemPool",
+              "hipMemCreate", "hipMemMap", "hipMallocAsync", "hipMemAllocHost")
+
+
+def test_library_imports_no_allocator():
+    import shutil
+    import subprocess
+
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    path = os.path.join(REPO, "exact_tiled_attention_15_amd", "libattn.so")
+    out = subprocess.run([nm, "-D", "--undefined-only", path], capture_output=True, text=True, check=True).stdout
+    imported = {line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip()}
+    assert "hipLaunchKernel" in imported  # the listing is the library's real import table
+    bad = sorted(s for s in imported if s.startswith(ALLOCATORS))
+    assert not bad, f"libattn.so imports allocating entry points: {bad}"
