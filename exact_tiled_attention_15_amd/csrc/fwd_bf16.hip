@@ -457,11 +457,13 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
       // The stage is refilled next (the next block's second tile, or its
       // first tile and Q).
       __syncthreads();
+      // Non-temporal: this kernel never reads O back, and 64 KiB per block of
+      // it left in L2 would push out K/V lines other workgroups still stream.
       uint16_t* ob = (uint16_t*)p.o + ((int64_t)b.bh * Nq + b.q0) * D;
 #pragma unroll
       for (int n = 0; n < NO; ++n) {
         const int r = n * RPN + rr;
-        if (b.q0 + r < Nq) *(u32x4*)(ob + (int64_t)r * D + 8 * ch) = ov[n];
+        if (b.q0 + r < Nq) __builtin_nontemporal_store(ov[n], (u32x4*)(ob + (int64_t)r * D + 8 * ch));
       }
     } else if (my_q < Nq) {
       const int64_t row = (int64_t)b.bh * Nq + my_q;
