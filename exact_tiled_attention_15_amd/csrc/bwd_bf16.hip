@@ -20,17 +20,19 @@
 //                     K^T stored transposed and key-permuted in LDS exactly as
 //                     the forward stores V^T (common.h).
 //   bwd_dkdv_kernel   key rows stationary (4 wavefronts x 32 keys, one per
-//                     SIMD, so the two fp32 accumulators fit); Q, Q^T, dO,
-//                     dO^T, LSE and D stream through LDS in 64-query tiles.
-//                     S = Q K^T and dP = dO V^T put one key per lane;
+//                     SIMD, so the two fp32 accumulators fit); Q and dO rows
+//                     stream through LDS in 64-query tiles by buffer->LDS
+//                     transfers (no registers on the way), LSE and D beside
+//                     them.  S = Q K^T and dP = dO V^T put one key per lane;
 //                     dV^T += dO^T P and dK^T += Q^T dS take P and dS from the
-//                     accumulators, with dO^T and Q^T stored transposed and
-//                     query-permuted.
+//                     accumulators, their dO^T and Q^T fragments read from the
+//                     same row tiles by transposing reads (ds_read_b64_tr_b16).
 // Probabilities and dS are rounded to bf16 for the products, accumulations are
 // fp32.  Masked (query, key) pairs get p = 0 by selection, so any finite
 // scale works.  Staging loads past the tensor ends read the last row instead
-// (unconditional loads, so none waits for another); every (query, key) pair
-// they form is masked, so its P and dS are exactly 0.
+// (unconditional loads, so none waits for another), or zero (the dK/dV
+// kernel's range-checked transfers); every (query, key) pair they form is
+// masked, so its P and dS are exactly 0.
 #include <type_traits>
 
 #include "common.h"
@@ -239,16 +241,23 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_kernel(BwdParams p, int nqb) {
 template <int D>
 struct DkvGeo {
   static constexpr int W = 4, THREADS = 64 * W, BK = 32 * W, BM = 64, QB = BM / 32;
-  static constexpr int KS = D * 2 + 16;                 // Q / dO row pitch
-  static constexpr int VTP = vt_pitch(BM);              // Q^T / dO^T row pitch
-  static constexpr int R_BYTES = BM * KS, T_BYTES = D * VTP;
-  static constexpr int STAGE = 2 * R_BYTES + 2 * T_BYTES + 2 * BM * 4;  // Q, dO, Q^T, dO^T, LSE2, D
+  static constexpr int KS = D * 2;                      // Q / dO row pitch (unpadded, chunks permuted)
+  static constexpr int R_BYTES = BM * KS;
+  static constexpr int STAGE = 2 * R_BYTES + 2 * BM * 4;  // Q, dO, LSE2, D
   static constexpr int LDS = 2 * STAGE;
-  static constexpr int QG = BM / 4;                     // 4-query groups per tile
-  static constexpr int STAGERS = QG * (D / 8);          // per tensor
-  static_assert(STAGERS <= THREADS, "one Q and one dO block per thread at most");
+  static constexpr int CPR = D / 8;                     // 16-byte chunks per row
+  static constexpr int RPT = 64 / CPR;                  // rows per wave-wide 1 KiB transfer
+  static constexpr int TPW = R_BYTES / 1024 / W;        // transfers per tensor and wavefront
+  static_assert(TPW * W * 1024 == R_BYTES, "Q / dO tile must be whole transfers per wavefront");
   static_assert(2 * BM <= THREADS, "LSE and D loaded by one thread each");
 };
+// Slot permutation of the Q / dO tiles: 16-byte chunk c of row r sits at slot
+// c ^ qslot(r).  Even values only, distinct over 8 consecutive rows (16-byte
+// row reads of 8 lanes at one chunk hit 8 bank groups) and over the 4 rows of
+// a transposing read's 16 lanes, whose two chunks c, c + 1 then land on 8
+// distinct slots.  d = 64 packs two rows per 256 bytes, so its rows pair up.
+template <int D>
+__device__ constexpr int qslot(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
 
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) {
@@ -296,53 +305,70 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) 
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dk[db] = dv[db] = (f32x16){};
 
-  // Staging: thread (dc, qgrp) holds queries 4*qgrp .. +3, columns 8*dc .. +7
-  // of Q and of dO; threads 0 .. BM-1 also fetch LSE2, BM .. 2BM-1 fetch D.
-  const bool stager = tid < G::STAGERS;
-  // Column chunk rotated by the query group: the 16 lanes of one row store
-  // (rows 4 apart) then cover all 16-byte bank groups instead of 4.
-  const int s_qg = tid % G::QG, s_dc = (tid / G::QG + s_qg) % (D / 8);
-  u32x4 qreg[4], dreg[4];
+  // Staging.  Q and dO rows go straight from global memory into LDS (buffer
+  // loads with an LDS destination, range-checked: rows past Nq read as zero
+  // and every pair they form is masked), rows whole, chunks permuted by
+  // qslot.  Wavefront w issues transfers w + W n, so each lane's row within a
+  // transfer, and with it its permuted source chunk, is one constant.
+  // Threads 0 .. BM-1 fetch LSE2, BM .. 2BM-1 fetch D, through registers.
+  const unsigned q_lane = [&]() {
+    const int row = G::RPT * wave + lane / G::CPR, j = lane % G::CPR;
+    return (unsigned)((lane / G::CPR) * G::KS + 16 * (j ^ qslot<D>(row)));
+  }();
+  const unsigned lds0 = lds_offset(smem);
   float sval = 0.f;
   const float* __restrict__ sbase = (tid < G::BM ? lseg : dltg) + (tid % G::BM);
   const float* sptr = sbase;
   auto stage_base = [&](int t) { return smem + (t & 1) * G::STAGE; };
   auto gload = [&](int t) {
-    if (stager) {
+    const int q0t = t * G::BM;
+    const unsigned nbytes = (unsigned)(max(0, min(G::BM, Nq - q0t)) * G::KS);
+    const i32x4 rq = buffer_rsrc_n(qg + (int64_t)q0t * D, nbytes);
+    const i32x4 rd = buffer_rsrc_n(dog + (int64_t)q0t * D, nbytes);
+    const unsigned sb = lds0 + (unsigned)((t & 1) * G::STAGE);
+    unsigned soff = __builtin_amdgcn_readfirstlane(1024u * wave);
+    unsigned lds = __builtin_amdgcn_readfirstlane(sb + 1024u * wave);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t off = (int64_t)min(t * G::BM + 4 * s_qg + r, Nq - 1) * D + s_dc * 8;
-        qreg[r] = *(const u32x4*)(qg + off);
-        dreg[r] = *(const u32x4*)(dog + off);
-      }
-    }
+    for (int n = 0; n < G::TPW; ++n) buf_lds16<1024 * G::W, 1024 * G::W>(rq, q_lane, soff, lds);
+    soff = __builtin_amdgcn_readfirstlane(1024u * wave);
+    lds = __builtin_amdgcn_readfirstlane(sb + (unsigned)G::R_BYTES + 1024u * wave);
+#pragma unroll
+    for (int n = 0; n < G::TPW; ++n) buf_lds16<1024 * G::W, 1024 * G::W>(rd, q_lane, soff, lds);
     if (tid < 2 * G::BM) {  // raw LSE or D; converted when staged
       // Full tiles read through a pointer carried across the tile loop, so
       // its registers are never recycled while the load is in flight (that
       // would cost a wait for every outstanding load); the last, ragged tile
       // clamps its row.
-      const int q0t = t * G::BM;
       if (q0t + G::BM <= Nq) sval = *(sptr + q0t);
       else sval = sbase[min(q0t + (tid % G::BM), Nq - 1) - (tid % G::BM)];
     }
   };
   auto lstore = [&](int t) {
     char* b = stage_base(t);
-    if (stager) {
-      store_rows(b, G::KS, 4 * s_qg, s_dc, qreg);
-      store_rows(b + G::R_BYTES, G::KS, 4 * s_qg, s_dc, dreg);
-      store_vt(b + 2 * G::R_BYTES, G::VTP, 8 * s_dc, s_qg, qreg);
-      store_vt(b + 2 * G::R_BYTES + G::T_BYTES, G::VTP, 8 * s_dc, s_qg, dreg);
-    }
     if (tid < 2 * G::BM) {
       // LSE in base 2 (rows without keys, LSE = -inf, are masked anyway), or D
       const float v = tid < G::BM ? (sval == -INFINITY ? 0.f : sval * kLog2e) : sval;
-      ((float*)(b + 2 * G::R_BYTES + 2 * G::T_BYTES))[tid] = v;
+      ((float*)(b + 2 * G::R_BYTES))[tid] = v;
     }
   };
 
-  const int r_off = r32 * G::KS + g * 16;
-  const int t_off = r32 * G::VTP + g * 16;
+  // Row fragment (S = Q K^T, dP = dO V^T; A operand): row r32 of a 32-row
+  // block, chunk 2kk + g at slot (2kk + g) ^ qslot(r32) = 2kk ^ (g ^ qslot(r32)).
+  const int r_off = r32 * G::KS;
+  const int r_x = 16 * (g ^ qslot<D>(r32));
+  // Transposed fragment (dV^T += dO^T P, dK^T += Q^T dS; A operand: row d =
+  // 32 db + l % 32, queries 4g .. 4g+3 and 8+4g .. 8+4g+3 of a 16-query half
+  // in P's order) by two transposing reads: lane (q, m, e) = ((l / 16) % 2,
+  // (l % 16) / 4, l % 4) addresses query 4g + m (and 8 on), columns 32 db +
+  // 16 q + 4 e, i.e. chunk 4 db + 2 q + e / 2, byte 8 (e % 2).  The slot
+  // permutation is even and the row's part of it is the same 8 rows on, so
+  // chunk (4 db + y) ^ x = (4 db ^ (x & ~3)) + (y ^ (x & 3)): the column block
+  // enters as an XOR of 64 db on the byte address.
+  const unsigned t_lane = [&]() {
+    const int vq = (lane >> 4) & 1, vm = (lane & 15) >> 2, ve = lane & 3;
+    const int row = 4 * g + vm, x = qslot<D>(row), y = 2 * vq + (ve >> 1);
+    return (unsigned)(row * G::KS + 16 * (x & ~3) + 16 * (y ^ (x & 3)) + 8 * (ve & 1));
+  }();
 
   if (ntiles > t0) {
     gload(t0);
@@ -361,10 +387,9 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) 
     if (more) gload(t + 1);
     const char* qb = stage_base(t);
     const char* dob = qb + G::R_BYTES;
-    const char* qtb = qb + 2 * G::R_BYTES;
-    const char* dotb = qtb + G::T_BYTES;
-    const float* l2 = (const float*)(dotb + G::T_BYTES);
+    const float* l2 = (const float*)(qb + 2 * G::R_BYTES);
     const float* dl = l2 + G::BM;
+    const unsigned qb_lds = lds0 + (unsigned)((t & 1) * G::STAGE);
     // The tile's 64 MFMAs, in issue order (h: 32-query block):
     //   0 .. 31   S[h] and dP[h], h = i / 16, k-slice (i / 2) % 8, S / dP
     //   32 .. 63  dV^T and dK^T, h = (i - 32) / 16, then half, column block,
@@ -392,11 +417,15 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) 
     auto frag = [&](int i) {
       if (i < NSD) {
         const int h = i / PER, kk = (i / 2) % (D / 16), w = i % 2;
-        return *(const bf16x8*)((w ? dob : qb) + h * 32 * G::KS + r_off + kk * 32);
+        return *(const bf16x8*)((w ? dob : qb) + h * 32 * G::KS + r_off + ((kk * 32) ^ r_x));
       }
       const int j = i - NSD, h = j / PER, half = (j / 2) / (D / 32) % 2, db = (j / 2) % (D / 32), w = j % 2;
-      const int off = db * 32 * G::VTP + t_off + (32 * h + 16 * half) * 2;
-      return *(const bf16x8*)((w ? qtb : dotb) + off);
+      // w = 0: dO^T (dV), w = 1: Q^T (dK)
+      const unsigned a = ((qb_lds + (unsigned)(w ? 0 : G::R_BYTES) + t_lane) ^ (unsigned)(64 * db)) +
+                         (unsigned)((32 * h + 16 * half) * G::KS);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(a + 8 * G::KS));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     f32x16 s[G::QB], dp[G::QB];
     float pr[16], ds[16];
@@ -451,6 +480,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) 
       __builtin_amdgcn_sched_barrier(0);
     });
     if (more) lstore(t + 1);
+    __builtin_amdgcn_s_waitcnt(0);  // the transfers of tile t + 1 (vmcnt only counts them)
     __syncthreads();
   };
   // Tiles t_lo .. t_hi-1 are all-live: every key of the block exists, the
