@@ -12,13 +12,13 @@
 //
 // Three kernels:
 //   bwd_delta_kernel  D_i = dO_i . O_i (fp32), one pass over dO and O.
-//   bwd_dq_kernel     query rows stationary (8 wavefronts x 32 rows); K, K^T
-//                     and V stream through LDS in 64-key tiles.  S^T = K Q^T
-//                     and dP^T = V dO^T put one query per lane, so LSE_i and
-//                     D_i are per-lane scalars; dQ^T += K^T dS^T takes dS^T
-//                     straight from the accumulators as the B operand, with
-//                     K^T stored transposed and key-permuted in LDS exactly as
-//                     the forward stores V^T (common.h).
+//   bwd_dq_kernel     query rows stationary (8 wavefronts x 32 rows); K and V
+//                     rows stream through LDS in 64-key tiles by buffer->LDS
+//                     transfers.  S^T = K Q^T and dP^T = V dO^T put one query
+//                     per lane, so LSE_i and D_i are per-lane scalars;
+//                     dQ^T += K^T dS^T takes dS^T straight from the
+//                     accumulators as the B operand, its K^T fragments read
+//                     from the K row tile by transposing reads.
 //   bwd_dkdv_kernel   key rows stationary (4 wavefronts x 32 keys, one per
 //                     SIMD, so the two fp32 accumulators fit); Q and dO rows
 //                     stream through LDS in 64-query tiles by buffer->LDS
@@ -29,10 +29,9 @@
 //                     same row tiles by transposing reads (ds_read_b64_tr_b16).
 // Probabilities and dS are rounded to bf16 for the products, accumulations are
 // fp32.  Masked (query, key) pairs get p = 0 by selection, so any finite
-// scale works.  Staging loads past the tensor ends read the last row instead
-// (unconditional loads, so none waits for another), or zero (the dK/dV
-// kernel's range-checked transfers); every (query, key) pair they form is
-// masked, so its P and dS are exactly 0.
+// scale works.  Rows past the tensor ends read as zero through the range-
+// checked transfers (LSE and D: the last row); every (query, key) pair they
+// form is masked, so its P and dS are exactly 0.
 #include <type_traits>
 
 #include "common.h"
@@ -48,12 +47,6 @@ __device__ inline bf16x8 pack8(const float* x) {
   typedef float f32x8 __attribute__((ext_vector_type(8)));
   f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
   return __builtin_convertvector(v, bf16x8);
-}
-
-// Row-major tile store: rows r0 .. r0+3 (4 x 16 bytes of w) at column chunk dc.
-__device__ inline void store_rows(char* tile, int pitch, int r0, int dc, const u32x4 (&w)[4]) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) *(u32x4*)(tile + (r0 + r) * pitch + dc * 16) = w[r];
 }
 
 }  // namespace
@@ -80,18 +73,27 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(BwdParams p, int64_t row
   if (row < rows && c == 0) p.delta[row] = acc;
 }
 
+// Slot permutation of the row tiles that both kernels stage (K and V for dQ,
+// Q and dO for dK/dV): 16-byte chunk c of row r sits at slot
+// c ^ qslot(r).  Even values only, distinct over 8 consecutive rows (16-byte
+// row reads of 8 lanes at one chunk hit 8 bank groups) and over the 4 rows of
+// a transposing read's 16 lanes, whose two chunks c, c + 1 then land on 8
+// distinct slots.  d = 64 packs two rows per 256 bytes, so its rows pair up.
+template <int D>
+__device__ constexpr int qslot(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
+
 // --------------------------------------------------------------------- dQ
 template <int D>
 struct DqGeo {
   static constexpr int W = 8, THREADS = 64 * W, BM = 32 * W, BN = 64, KB = BN / 32;
-  static constexpr int KS = D * 2 + 16;                 // K / V row pitch
-  static constexpr int VTP = vt_pitch(BN);              // K^T row pitch
-  static constexpr int K_BYTES = BN * KS, KT_BYTES = D * VTP, V_BYTES = BN * KS;
-  static constexpr int STAGE = K_BYTES + KT_BYTES + V_BYTES;
+  static constexpr int KS = D * 2;                      // K / V row pitch (unpadded, chunks permuted)
+  static constexpr int K_BYTES = BN * KS, V_BYTES = BN * KS;
+  static constexpr int STAGE = K_BYTES + V_BYTES;
   static constexpr int LDS = 2 * STAGE;
-  static constexpr int KG = BN / 4;                     // 4-key groups per tile
-  static constexpr int STAGERS = KG * (D / 8);          // per tensor (K or V)
-  static_assert(2 * STAGERS <= THREADS, "one K and one V stager per thread at most");
+  static constexpr int CPR = D / 8;                     // 16-byte chunks per row
+  static constexpr int RPT = 64 / CPR;                  // rows per wave-wide 1 KiB transfer
+  static constexpr int TPW = K_BYTES / 1024 / W;        // transfers per tensor and wavefront
+  static_assert(TPW >= 1 && TPW * W * 1024 == K_BYTES, "K / V tile must be whole transfers per wavefront");
 };
 
 template <int D, bool CAUSAL>
@@ -143,46 +145,54 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_kernel(BwdParams p, int nqb) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc[db] = (f32x16){};
 
-  // Staging: thread (tensor, dc, kgrp) holds keys 4*kgrp .. +3, columns 8*dc .. +7.
-  const int st = tid / G::STAGERS;  // 0: K, 1: V, 2+: idle
-  // The column chunk is rotated by the key group so that the 16 lanes of one
-  // row store (rows 4 apart) cover all 16-byte bank groups instead of 4.
-  const int su = tid - st * G::STAGERS, s_kg = su % G::KG, s_dc = (su / G::KG + s_kg) % (D / 8);
-  u32x4 sreg[4];
+  // Staging: K and V rows go straight from global memory into LDS (range-
+  // checked buffer transfers: keys past Nk read as zero and are masked), rows
+  // whole, chunks permuted by qslot; wavefront w issues transfers w + W n, so
+  // each lane's permuted source chunk is one constant.
+  const unsigned kv_lane = [&]() {
+    const int row = G::RPT * wave + lane / G::CPR, j = lane % G::CPR;
+    return (unsigned)((lane / G::CPR) * G::KS + 16 * (j ^ qslot<D>(row)));
+  }();
+  const unsigned lds0 = lds_offset(smem);
   auto stage_base = [&](int t) { return smem + (t & 1) * G::STAGE; };
   auto gload = [&](int t) {
-    if (st > 1) return;
-    const uint16_t* src = st == 0 ? kg : vg;
+    const int k0t = t * G::BN;
+    const unsigned nbytes = (unsigned)(max(0, min(G::BN, Nk - k0t)) * G::KS);
+    const i32x4 rk = buffer_rsrc_n(kg + (int64_t)k0t * D, nbytes);
+    const i32x4 rv = buffer_rsrc_n(vg + (int64_t)k0t * D, nbytes);
+    const unsigned sb = lds0 + (unsigned)((t & 1) * G::STAGE);
+    unsigned soff = __builtin_amdgcn_readfirstlane(1024u * wave);
+    unsigned lds = __builtin_amdgcn_readfirstlane(sb + 1024u * wave);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = min(t * G::BN + 4 * s_kg + r, Nk - 1);
-      sreg[r] = *(const u32x4*)(src + (int64_t)key * D + s_dc * 8);
-    }
-  };
-  auto lstore = [&](int t) {
-    char* b = stage_base(t);
-    if (st == 0) {
-      store_rows(b, G::KS, 4 * s_kg, s_dc, sreg);
-      store_vt(b + G::K_BYTES, G::VTP, 8 * s_dc, s_kg, sreg);
-    } else if (st == 1) {
-      store_rows(b + G::K_BYTES + G::KT_BYTES, G::KS, 4 * s_kg, s_dc, sreg);
-    }
+    for (int n = 0; n < G::TPW; ++n) buf_lds16<1024 * G::W, 1024 * G::W>(rk, kv_lane, soff, lds);
+    soff = __builtin_amdgcn_readfirstlane(1024u * wave);
+    lds = __builtin_amdgcn_readfirstlane(sb + (unsigned)G::K_BYTES + 1024u * wave);
+#pragma unroll
+    for (int n = 0; n < G::TPW; ++n) buf_lds16<1024 * G::W, 1024 * G::W>(rv, kv_lane, soff, lds);
   };
 
-  const int r_off = r32 * G::KS + g * 16;    // row r32 of a 32-row block, 16-byte slice g
-  const int t_off = r32 * G::VTP + g * 16;   // transposed tile: row r32 of a 32-row block, slot 8g
+  // Row fragment (S^T = K Q^T, dP^T = V dO^T; A operand): row r32 of a 32-key
+  // block, chunk 2kk + g at slot 2kk ^ (g ^ qslot(r32)).
+  const int r_off = r32 * G::KS;
+  const int r_x = 16 * (g ^ qslot<D>(r32));
+  // K^T fragment (dQ^T += K^T dS^T; A operand: row d = 32 db + l % 32, keys
+  // 4g .. 4g+3 and 8+4g .. 8+4g+3 of a 16-key half in dS's order) by two
+  // transposing reads, addressed as in the dK/dV kernel below.
+  const unsigned t_lane = [&]() {
+    const int vq = (lane >> 4) & 1, vm = (lane & 15) >> 2, ve = lane & 3;
+    const int row = 4 * g + vm, x = qslot<D>(row), y = 2 * vq + (ve >> 1);
+    return (unsigned)(row * G::KS + 16 * (x & ~3) + 16 * (y ^ (x & 3)) + 8 * (ve & 1));
+  }();
 
-  if (ntiles > 0) {
-    gload(0);
-    lstore(0);
-  }
+  if (ntiles > 0) gload(0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const bool more = t + 1 < ntiles;
     if (more) gload(t + 1);
     const char* kb = stage_base(t);
-    const char* ktb = kb + G::K_BYTES;
-    const char* vb = ktb + G::KT_BYTES;
+    const char* vb = kb + G::K_BYTES;
+    const unsigned kb_lds = lds0 + (unsigned)((t & 1) * G::STAGE);
     // Tiles in which every (query, key) pair of this wavefront is live skip
     // the per-element mask; only the probabilities sit under the branch.
     const bool full = __builtin_amdgcn_readfirstlane(
@@ -192,9 +202,9 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_kernel(BwdParams p, int nqb) {
       f32x16 s = (f32x16){}, dp = (f32x16){};
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 a = *(const bf16x8*)(kb + h * 32 * G::KS + r_off + kk * 32);
+        const bf16x8 a = *(const bf16x8*)(kb + h * 32 * G::KS + r_off + ((kk * 32) ^ r_x));
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s, 0, 0, 0);
-        const bf16x8 b = *(const bf16x8*)(vb + h * 32 * G::KS + r_off + kk * 32);
+        const bf16x8 b = *(const bf16x8*)(vb + h * 32 * G::KS + r_off + ((kk * 32) ^ r_x));
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, dof[kk], dp, 0, 0, 0);
       }
       float pr[16], ds[16];
@@ -217,11 +227,14 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_kernel(BwdParams p, int nqb) {
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const bf16x8 a = *(const bf16x8*)(ktb + db * 32 * G::VTP + t_off + (32 * h + 16 * half) * 2);
+          const unsigned ad = ((kb_lds + t_lane) ^ (unsigned)(64 * db)) + (unsigned)((32 * h + 16 * half) * G::KS);
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)ad);
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(ad + 8 * G::KS));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pd[half], acc[db], 0, 0, 0);
         }
     }
-    if (more) lstore(t + 1);
+    __builtin_amdgcn_s_waitcnt(0);  // the transfers of tile t + 1 (vmcnt only counts them)
     __syncthreads();
   }
 
@@ -251,13 +264,7 @@ struct DkvGeo {
   static_assert(TPW * W * 1024 == R_BYTES, "Q / dO tile must be whole transfers per wavefront");
   static_assert(2 * BM <= THREADS, "LSE and D loaded by one thread each");
 };
-// Slot permutation of the Q / dO tiles: 16-byte chunk c of row r sits at slot
-// c ^ qslot(r).  Even values only, distinct over 8 consecutive rows (16-byte
-// row reads of 8 lanes at one chunk hit 8 bank groups) and over the 4 rows of
-// a transposing read's 16 lanes, whose two chunks c, c + 1 then land on 8
-// distinct slots.  d = 64 packs two rows per 256 bytes, so its rows pair up.
-template <int D>
-__device__ constexpr int qslot(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
+
 
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) {
