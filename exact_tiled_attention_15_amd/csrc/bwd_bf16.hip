@@ -234,7 +234,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dq_kernel(BwdParams p, int nqb) {
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pd[half], acc[db], 0, 0, 0);
         }
     }
-    __builtin_amdgcn_s_waitcnt(0);  // the transfers of tile t + 1 (vmcnt only counts them)
+    __builtin_amdgcn_s_waitcnt(0);  // tile t + 1's transfers: counted by vmcnt only, not covered by the barrier
     __syncthreads();
   }
 
@@ -487,7 +487,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) 
       __builtin_amdgcn_sched_barrier(0);
     });
     if (more) lstore(t + 1);
-    __builtin_amdgcn_s_waitcnt(0);  // the transfers of tile t + 1 (vmcnt only counts them)
+    __builtin_amdgcn_s_waitcnt(0);  // tile t + 1's transfers: counted by vmcnt only, not covered by the barrier
     __syncthreads();
   };
   // Tiles t_lo .. t_hi-1 are all-live: every key of the block exists, the

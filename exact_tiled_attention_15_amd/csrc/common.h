@@ -108,10 +108,10 @@ __device__ inline int sched_block(int k, int w, int G, int n) {
   return r < n ? r : -1;
 }
 
-// Causal persistent schedule in pairs.  Query block j of a slice sees j + 1
-// diagonal-aligned key ranges of the block size and block nqb-1-j sees nqb - j,
-// so the pair (nqb-1-j, j) always carries nqb + 1 of them: a workgroup that
-// takes whole pairs gets an exact share of the tiles.  Workgroup w (XCD
+// Causal persistent schedule in pairs.  With a square causal mask, query
+// block j of a slice sees the first (j + 1) * BM keys and block nqb-1-j the
+// first (nqb - j) * BM, so the pair (nqb-1-j, j) always covers (nqb + 1) * BM
+// keys: a workgroup that takes whole pairs gets an exact share of the tiles.  Workgroup w (XCD
 // w % 8) takes units u = r * G/8 + w / 8, r = 0, 1, ..., of its XCD's
 // (BH/8) * (nqb/2) units; unit u is pair u % (nqb/2) of the XCD's slice
 // u / (nqb/2), heavier block first.  The workgroups of an XCD that run at the

@@ -457,8 +457,8 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_bf16_kernel(FwdParams p) {
       // The stage is refilled next (the next block's second tile, or its
       // first tile and Q).
       __syncthreads();
-      // Non-temporal: this kernel never reads O back, and 64 KiB per block of
-      // it left in L2 would push out K/V lines other workgroups still stream.
+      // Non-temporal: this kernel never reads O back, and a block's O left in
+      // L2 would push out K/V lines that other workgroups still stream.
       uint16_t* ob = (uint16_t*)p.o + ((int64_t)b.bh * Nq + b.q0) * D;
 #pragma unroll
       for (int n = 0; n < NO; ++n) {
