@@ -32,6 +32,7 @@
 // scale works.  Rows past the tensor ends read as zero through the range-
 // checked transfers (LSE and D: the last row); every (query, key) pair they
 // form is masked, so its P and dS are exactly 0.
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -522,6 +523,33 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p, int nkb) 
 }
 
 // --------------------------------------------------------------- launcher
+// The dQ and dK/dV kernels read the same inputs and write disjoint outputs, so
+// dQ runs on a second stream, concurrently with dK/dV: each kernel's last,
+// partly empty round of workgroups then shares the chip with the other's
+// work.  Per device: that stream and the fork / join events, created on the
+// first call and kept until the process ends.  The mutex makes each call's
+// record / wait sequence atomic, so concurrent callers cannot interleave on
+// the shared events.
+namespace {
+struct BwdSide {
+  std::mutex mu;
+  bool ready = false;
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kBwdMaxDevices = 64;
+BwdSide g_bwd_side[kBwdMaxDevices];
+
+hipError_t side_init(BwdSide& c) {
+  if (c.ready) return hipSuccess;
+  if (hipError_t e = hipStreamCreateWithFlags(&c.stream, hipStreamNonBlocking)) return e;
+  if (hipError_t e = hipEventCreateWithFlags(&c.fork, hipEventDisableTiming)) return e;
+  if (hipError_t e = hipEventCreateWithFlags(&c.join, hipEventDisableTiming)) return e;
+  c.ready = true;
+  return hipSuccess;
+}
+}  // namespace
+
 template <int D>
 static hipError_t launch_bwd_d(const BwdParams& p, bool causal, hipStream_t s) {
   const int64_t rows = (int64_t)p.BH * p.Nq;
@@ -531,16 +559,27 @@ static hipError_t launch_bwd_d(const BwdParams& p, bool causal, hipStream_t s) {
   const int nkb = (p.Nk + DkvGeo<D>::BK - 1) / DkvGeo<D>::BK;
   const int nqb = (p.Nq + DqGeo<D>::BM - 1) / DqGeo<D>::BM;
   const dim3 gkv((unsigned)(nkb * p.BH)), gq((unsigned)(nqb * p.BH));
-  if (causal) {
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return e;
+  if (dev < 0 || dev >= kBwdMaxDevices) return hipErrorInvalidDevice;
+  BwdSide& c = g_bwd_side[dev];
+  std::lock_guard<std::mutex> lock(c.mu);
+  if (hipError_t e = side_init(c)) return e;
+  // dQ on the side stream once D is written; the caller's stream waits for it.
+  if (hipError_t e = hipEventRecord(c.fork, s)) return e;
+  if (hipError_t e = hipStreamWaitEvent(c.stream, c.fork, 0)) return e;
+  if (causal)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), gq, dim3(DqGeo<D>::THREADS), 0, c.stream, p, nqb);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), gq, dim3(DqGeo<D>::THREADS), 0, c.stream, p, nqb);
+  if (hipError_t e = hipGetLastError()) return e;
+  if (hipError_t e = hipEventRecord(c.join, c.stream)) return e;
+  if (causal)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), gkv, dim3(DkvGeo<D>::THREADS), 0, s, p, nkb);
-    if (hipError_t e = hipGetLastError()) return e;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), gq, dim3(DqGeo<D>::THREADS), 0, s, p, nqb);
-  } else {
+  else
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), gkv, dim3(DkvGeo<D>::THREADS), 0, s, p, nkb);
-    if (hipError_t e = hipGetLastError()) return e;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), gq, dim3(DqGeo<D>::THREADS), 0, s, p, nqb);
-  }
-  return hipGetLastError();
+  if (hipError_t e = hipGetLastError()) return e;
+  return hipStreamWaitEvent(s, c.join, 0);
 }
 
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t s) {

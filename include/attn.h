@@ -20,12 +20,14 @@
  *    host-resident K/V blocks of attn_fwd_ring_host).  The library allocates no
  *    memory and never synchronises the host: each call validates its arguments
  *    on the host, enqueues its kernels on `stream` (a hipStream_t; NULL means
- *    the default stream) and returns.  Global state is limited to two caches
+ *    the default stream) and returns.  Global state is limited to three caches
  *    that live until the process ends and never change a result: each device's
  *    compute-unit count (read once, used to size the W4A16 grid and the bf16
- *    forward's persistent grid), and
- *    attn_fwd_ring_host's per-device copy stream with five events, created on
- *    that entry point's first call on the device and guarded by a mutex.
+ *    forward's persistent grid), attn_fwd_ring_host's per-device copy stream
+ *    with five events, and attn_bwd's per-device side stream with two events;
+ *    each stream is created on its entry point's first call on the device and
+ *    guarded by a mutex, and work on it is joined back to `stream` before the
+ *    call returns.
  *  - Layout: contiguous [B, H, N, d] row-major, d innermost; per-row outputs
  *    (lse, m, l) are contiguous [B, H, N].  Q/K/V/O pointers must be 16-byte
  *    aligned; per-row pointers 4-byte aligned.  Outputs must not alias inputs.
@@ -159,6 +161,9 @@ attn_status attn_merge(float* o_acc, float* m_acc, float* l_acc,
  *                   floats (receives D), owned by the caller
  * causal and scale as in attn_fwd (any finite scale).  Products run on bf16
  * matrix cores with fp32 accumulation; P and dS are rounded to bf16 for them.
+ * The dQ kernel runs on the library's side stream for the device, after D is
+ * written and concurrently with the dK/dV kernel; `stream` waits for it, so
+ * every output is complete for work enqueued on `stream` after the call.
  * Errors: as attn_fwd, plus ATTN_ERR_INVALID for a NULL lse or work.
  */
 size_t attn_bwd_work_floats(int B, int H, int Nq);
