@@ -278,7 +278,12 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
   // ---- staging.  K codes go straight into LDS (fp8 form; the pad slot of a
   // row re-reads chunk 0) or through registers, widened to fp16 (fp16 form).
   // V: thread (dc, kgrp) takes keys 4*kgrp .. +3 of columns 8*dc .. +7
-  // (8 codes each), widens them to fp16 and stores them transposed.
+  // (8 codes each), widens them to fp16 and stores them transposed.  In the
+  // fp8 form V runs two tiles ahead: tile t+1's codes, loaded during
+  // iteration t-1, are widened and stored right after iteration t's Q.K
+  // products (where the SIMD's other wavefront keeps the matrix cores busy),
+  // and tile t+2's loads go out then and stay in flight across the tile
+  // barrier (vmcnt(4)), so they have a whole iteration to arrive.
   const int v_dc = tid / G::KG, v_kg = tid % G::KG;
   const bool v_stager = tid < G::V_THREADS;
   u32x2 vreg[4];
@@ -345,7 +350,8 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = k0 + 4 * v_kg + r;
-        vreg[r] = key < Nk ? *(const u32x2*)(src + r * D) : (u32x2){0u, 0u};
+        const u32x2 x = *(const u32x2*)(vg + (int64_t)min(key, Nk - 1) * D + v_dc * 8);
+        vreg[r] = key < Nk ? x : (u32x2){0u, 0u};
       }
     }
   };
@@ -431,6 +437,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
     store_k(0);
     lstore_v(0);
   }
+  if (!QK16 && ntiles > 0) gload_v(min(1, ntiles - 1));
   publish();
   if constexpr (!QK16) {
     // Q fragment (B operand): row my_q, bytes 64 kk + 32 g .. +32 = chunks
@@ -471,8 +478,20 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
     const float ks_t = ks_next, vs_t = vs_next;
     if (more) {
       load_k(t + 1);
-      gload_v(t + 1);
+      if (QK16) gload_v(t + 1);
       scale_pair(t + 1, ks_next, vs_next);
+    }
+    f32x16 s[G::KB];
+    if (t < wtiles) qk(kstage(t), s);
+    // fp8 form: tile t+1's V (buffer (t+1) & 1, last read in iteration t-1)
+    // from registers to LDS, then tile t+2's loads (the last tile again at
+    // the end of the slice, unused).  The next tile's scales are consumed
+    // first, so that the V loads are the only ones in flight at the barrier.
+    const int v_next = min(t + 2, ntiles - 1);
+    if constexpr (!QK16) {
+      if (more) lstore_v(t + 1);
+      asm volatile("" ::"v"(ks_next), "v"(vs_next));
+      gload_v(v_next);
     }
     if (t < wtiles) {
       const int k0 = t * BN;
@@ -481,8 +500,6 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
       const float vfold = __log2f(sv * inv_svmax);  // <= 0
       const float vunfold = svmax * __builtin_amdgcn_rcpf(sv);
 
-      f32x16 s[G::KB];
-      qk(kstage(t), s);
       if (k0 + BN > wmask_from) mask(s, k0);
 
       float mx = s[0][0];
@@ -636,11 +653,19 @@ __global__ void __launch_bounds__(64 * W, 8 / W) fwd_fp8_kernel(FwdParams p) {
         }
       }
       }
-    if (more) {
+    if (QK16 && more) {
       store_k(t + 1);
       lstore_v(t + 1);
     }
-    publish();
+    // A whole tile's V loads are four unconditional instructions, issued
+    // after every other vector memory access of the iteration, so vmcnt(4)
+    // covers this iteration's K transfers; a partial tile's loads are
+    // predicated per key (a wavefront may issue fewer), so they are waited
+    // for in full, as are the other forms' stages.
+    if (!QK16 && v_stager && (v_next + 1) * BN <= Nk)
+      asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+      publish();
   }
 
   const float l_tot = halves_sum(l_lane);
